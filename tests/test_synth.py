@@ -1,0 +1,42 @@
+"""The seeded generator: determinism, shapes and the intended distributions."""
+import numpy as np
+
+import oracle
+import synth
+
+
+def test_deterministic_and_seed_dependent():
+    w = synth.scaled(synth.TRAIN_TOP2, T=5000, H=64)
+    a, b = synth.make_logits(w, 0), synth.make_logits(w, 0)
+    assert np.array_equal(a, b) and a.dtype == np.float32 and a.shape == (5000, 64)
+    assert not np.array_equal(a, synth.make_logits(w, 1))
+    xa, xb = synth.make_x(w, 0), synth.make_x(w, 0)
+    assert np.array_equal(xa, xb) and xa.dtype == np.uint16 and xa.shape == (5000, 64)
+
+
+def test_activation_distribution():
+    for w in (synth.TINY, synth.scaled(synth.TRAIN_TOP2, T=2048, H=256)):
+        v = oracle.decode16(synth.make_x(w, 0), w.act_dtype).astype(np.float64)
+        assert abs(v.mean()) < 0.02 and abs(v.std() - 1) < 0.02
+
+
+def test_cluster_pairs_bias_drives_top2():
+    w = synth.scaled(synth.TRAIN_TOP2, T=4096, H=8)
+    idx = oracle.topk_select(synth.make_logits(w, 0), 2)
+    pair = (idx[:, 0] // 2 == idx[:, 1] // 2)
+    assert pair.mean() > 0.4      # uniform logits would give about 1/63
+
+
+def test_zipf_skew():
+    w = synth.scaled(synth.TRAIN_TOP6, T=4096, H=8)
+    c = oracle.demand_vector(oracle.topk_select(synth.make_logits(w, 0), 6), 64)
+    assert c[0] > 5 * c.mean() and c[:8].sum() > c[32:].sum()
+
+
+def test_decode_replica_table():
+    rep = synth.replica_table(synth.DECODE)
+    assert rep.shape == (256, 2)
+    assert (rep[:, 0] == np.arange(256) // 32).all()
+    assert ((rep[:, 1] >= 0) == (np.arange(256) % 8 == 0)).all()
+    assert (rep[::8, 1] == (np.arange(0, 256, 8) // 32 + 4) % 8).all()
+    assert synth.replica_table(synth.TRAIN_TOP2) is None
