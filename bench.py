@@ -1,0 +1,222 @@
+"""Benchmark of the single-GPU MoE routing path on MI355X.
+
+One step = one pass of the whole path over one batch resident in HBM:
+route (top-k, gate weights, demand vector) -> greedy replica assignment ->
+layout (offsets, permutation, dedup) -> dispatch -> expert stand-in ->
+combine. The headline is dispatch+combine GB/s of algorithmic bytes,
+2 (1 + k) T H b, over the two kernels' HIP-event durations, and routed rows/s
+(T k rows over the same time). By default the 256 MB Infinity Cache and the L2s
+are flushed (a 1 GiB fill) before the dispatch and before the combine, outside
+their event brackets, so both read from HBM.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine HBM GB/s (% of peak) and routed rows/s at T=16384,E=64,top-2"
+PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+DEFAULT_WORKLOAD = "train_T16384_E64_k2_H4096_bf16_clustered"
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+FLUSH_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--warm-cache", action="store_true", help="no cache flush before dispatch/combine")
+    ap.add_argument("--cpu-tokens", type=int, default=1 << 30,
+                    help="tokens in the oracle's CPU-baseline sample (0 = skip; default all)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle's timed stages until this much CPU time is spent")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "combine_router_topk_amd", "csrc", "rows.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 PMC counters, if the
+    counters were taken on the current kernel source for this workload."""
+    try:
+        with open(PMC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("rows_hip_sha") != kernel_source_digest() or rec.get("workload") != workload:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seed: int, tokens: int, min_seconds: float):
+    """The oracle, as it stands, on the first `tokens` tokens of the same
+    workload: its dispatch and combine timed on the host (repeated until
+    `min_seconds` have been spent, at least once), in the metric's unit.
+    numpy runs these element-wise steps on one thread."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    sub = synth.scaled(w, T=min(tokens, w.T))
+    logits = synth.make_logits(w, seed)[:sub.T]
+    x = synth.make_x(w, seed)[:sub.T]
+    rep = synth.replica_table(w)
+    meta = oracle.route_and_layout(sub.T, sub.E, sub.k, sub.R, logits, rep)
+    secs, reps = 0.0, 0
+    while reps == 0 or secs < min_seconds:
+        t0 = time.perf_counter()
+        send = oracle.dispatch(x, meta["pos"], sub.k)
+        t1 = time.perf_counter()
+        y = oracle.expert_standin(send, meta["idx"].ravel()[meta["src"]], sub.E, sub.act_dtype)
+        t2 = time.perf_counter()
+        oracle.combine(y, meta["pos"], meta["w"], sub.k, sub.act_dtype)
+        t3 = time.perf_counter()
+        secs += (t1 - t0) + (t3 - t2)
+        reps += 1
+        del send, y
+    nbytes = sub.dispatch_combine_bytes() * reps
+    return {"value": round(nbytes / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {sub.T} of {w.T} tokens of {w.name}, {reps} passes; oracle dispatch + "
+                      f"fp64 combine ({secs:.2f} s for {nbytes} algorithmic bytes)",
+            "routed_rows_per_s": round(reps * sub.T * sub.k / secs, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the routing path is single-GPU; sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from combine_router_topk_amd import binding as B
+    from combine_router_topk_amd import path as P
+
+    w = synth.BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    logits = synth.make_logits(w, args.seed)
+    x = synth.make_x(w, args.seed)
+    rep = synth.replica_table(w)
+    tdt = torch.float16 if w.act_dtype == synth.F16 else torch.bfloat16
+    p = B.make_problem(w.T, w.E, w.k, w.H, w.R, w.act_dtype)
+    b = P.allocate(p, torch.from_numpy(logits), torch.from_numpy(x.view(np.int16)).view(tdt),
+                   None if rep is None else torch.from_numpy(rep), device=dev)
+    flush = None if args.warm_cache else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = []
+
+    def step(record: bool):
+        P.route(b)
+        P.assign(b)
+        P.layout(b)
+        if flush is not None:
+            flush.fill_(1.0)
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        e0.record()
+        P.dispatch(b)
+        e1.record()
+        P.standin(b)
+        if flush is not None:
+            flush.fill_(2.0)
+        e2.record()
+        P.combine(b)
+        e3.record()
+        if record:
+            marks.append((e0, e1, e2, e3))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    disp_ms = float(np.mean([a.elapsed_time(b_) for a, b_, _, _ in marks]))
+    comb_ms = float(np.mean([c.elapsed_time(d) for _, _, c, d in marks]))
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    half = (1 + w.k) * w.T * w.H * 2            # bytes of each of dispatch and combine
+    dc_bytes = 2 * half
+    dc_s = (disp_ms + comb_ms) / 1e3
+    value = dc_bytes / dc_s / 1e9
+    dom, dom_ms = ("dispatch_kernel", disp_ms) if disp_ms >= comb_ms else ("combine_kernel", comb_ms)
+    achieved = half / (dom_ms / 1e3) / 1e9
+    traffic = traffic_from_profiles(dom, w.name)
+
+    # a plain device copy of the dispatch's byte count, as the achievable-bandwidth reference
+    cp_src = torch.empty(half // 4, dtype=torch.int16, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    cp_ms = []
+    for i in range(6):
+        if flush is not None:
+            flush.fill_(3.0)
+        a, c = ev(), ev()
+        a.record()
+        cp_dst.copy_(cp_src)
+        c.record()
+        if i > 0:
+            cp_ms.append((a, c))
+    torch.cuda.synchronize()
+    copy_gbps = 2 * cp_src.numel() * 2 / (np.mean([a.elapsed_time(c) for a, c in cp_ms]) / 1e3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "E": w.E, "k": w.k, "H": w.H, "R": w.R,
+                   "act": w.dtype_name, "seed": args.seed,
+                   "cache": "warm" if flush is None else "cold: 1 GiB fill before dispatch and before combine"},
+        "frac_of_peak": round(value / PEAK_GBPS, 4),
+        "routed_rows_per_s": round(w.T * w.k / dc_s, 1),
+        "stage_ms": {"dispatch": round(disp_ms, 4), "combine": round(comb_ms, 4)},
+        "dedup_rows": int(b.dedup.sum().item()),
+        "raw_rows": w.T * w.k,
+        "max_active_experts": int(b.active.max().item()),
+        "copy_reference_GBps": round(copy_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": traffic},
+    }
+    if args.cpu_tokens > 0:
+        res["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_tokens, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

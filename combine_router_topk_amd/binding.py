@@ -1,0 +1,184 @@
+"""ctypes binding of libmoe_route.so: one Python function per C entry point,
+same names, same argument order (see include/moe_route.h).
+
+Only argument marshalling happens here: torch tensors (device memory) become
+pointers, the stream becomes torch's current HIP stream unless given, and
+tensor sizes are checked against the problem so the library can never be
+handed a buffer shorter than the shape it is told about. Every step of the
+routing path runs in the HIP library; there is no fallback. If the library is
+missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_route.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F16, MOE_BF16 = 1, 2
+MOE_FLAG_GREEDY_ID_ORDER = 1 << 0
+MOE_FLAG_OUT_F32 = 1 << 1
+
+EXPORTED = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
+            "moe_route", "moe_assign_replicas", "moe_layout", "moe_dispatch",
+            "moe_expert_standin", "moe_combine")
+
+_TORCH_ACT = {MOE_F16: torch.float16, MOE_BF16: torch.bfloat16}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({_status_string(status)}): {detail}")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("R", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+    def __repr__(self):
+        return (f"Problem(T={self.T}, E={self.E}, k={self.k}, H={self.H}, R={self.R}, "
+                f"act_dtype={self.act_dtype}, flags={self.flags})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m combine_router_topk_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "moe_version": (i32, []),
+        "moe_status_string": (ctypes.c_char_p, [i32]),
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_workspace_bytes": (i32, [P, ctypes.POINTER(sz)]),
+        "moe_route": (i32, [P, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_assign_replicas": (i32, [P, vp, vp, i32, vp, vp, vp]),
+        "moe_layout": (i32, [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_dispatch": (i32, [P, vp, vp, vp, vp]),
+        "moe_expert_standin": (i32, [P, vp, vp, vp, vp, vp]),
+        "moe_combine": (i32, [P, vp, vp, vp, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+def _status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where, _lib.moe_last_error().decode())
+
+
+def make_problem(T: int, E: int, k: int, H: int, R: int, act_dtype: int, flags: int = 0) -> Problem:
+    return Problem(T, E, k, H, R, act_dtype, flags)
+
+
+def _ptr(t: torch.Tensor | None, dtype: torch.dtype | None, numel: int | None, name: str):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, need {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def moe_version() -> int:
+    return _lib.moe_version()
+
+
+def moe_status_string(status: int) -> str:
+    return _status_string(status)
+
+
+def moe_last_error() -> str:
+    return _lib.moe_last_error().decode()
+
+
+def moe_workspace_bytes(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.moe_workspace_bytes(ctypes.byref(p), ctypes.byref(n)), "moe_workspace_bytes")
+    return n.value
+
+
+def moe_route(p: Problem, logits, idx, w, counts, ws, stream=None) -> None:
+    n = p.T * p.k
+    _check(_lib.moe_route(ctypes.byref(p),
+                          _ptr(logits, torch.float32, p.T * p.E, "logits"),
+                          _ptr(idx, torch.int32, n, "idx"), _ptr(w, torch.float32, n, "w"),
+                          _ptr(counts, torch.int32, p.E, "counts"), _ptr(ws, None, None, "ws"),
+                          ws.numel() * ws.element_size(), _stream(stream)), "moe_route")
+
+
+def moe_assign_replicas(p: Problem, counts, rep, maxrep: int, assign, active, stream=None) -> None:
+    _check(_lib.moe_assign_replicas(ctypes.byref(p), _ptr(counts, torch.int32, p.E, "counts"),
+                                    _ptr(rep, torch.int32, p.E * maxrep if rep is not None else 0, "rep"),
+                                    maxrep, _ptr(assign, torch.int32, p.E, "assign"),
+                                    _ptr(active, torch.int32, p.R, "active"), _stream(stream)),
+           "moe_assign_replicas")
+
+
+def moe_layout(p: Problem, idx, assign, rep, maxrep: int, rank_of, expert_offsets, rank_offsets,
+               pos, src, dedup, ws, stream=None) -> None:
+    n = p.T * p.k
+    _check(_lib.moe_layout(ctypes.byref(p), _ptr(idx, torch.int32, n, "idx"),
+                           _ptr(assign, torch.int32, p.E, "assign"),
+                           _ptr(rep, torch.int32, p.E * maxrep if rep is not None else 0, "rep"),
+                           maxrep, _ptr(rank_of, torch.int32, p.E, "rank_of"),
+                           _ptr(expert_offsets, torch.int32, p.E, "expert_offsets"),
+                           _ptr(rank_offsets, torch.int32, p.R + 1, "rank_offsets"),
+                           _ptr(pos, torch.int32, n, "pos"), _ptr(src, torch.int32, n, "src"),
+                           _ptr(dedup, torch.int32, p.R, "dedup"), _ptr(ws, None, None, "ws"),
+                           ws.numel() * ws.element_size(), _stream(stream)), "moe_layout")
+
+
+def moe_dispatch(p: Problem, x, pos, send, stream=None) -> None:
+    act = _TORCH_ACT.get(p.act_dtype)
+    _check(_lib.moe_dispatch(ctypes.byref(p), _ptr(x, act, p.T * p.H, "x"),
+                             _ptr(pos, torch.int32, p.T * p.k, "pos"),
+                             _ptr(send, act, p.T * p.k * p.H, "send"), _stream(stream)),
+           "moe_dispatch")
+
+
+def moe_expert_standin(p: Problem, send, src, idx, y, stream=None) -> None:
+    act = _TORCH_ACT.get(p.act_dtype)
+    n = p.T * p.k
+    _check(_lib.moe_expert_standin(ctypes.byref(p), _ptr(send, act, n * p.H, "send"),
+                                   _ptr(src, torch.int32, n, "src"), _ptr(idx, torch.int32, n, "idx"),
+                                   _ptr(y, act, n * p.H, "y"), _stream(stream)),
+           "moe_expert_standin")
+
+
+def moe_combine(p: Problem, y, pos, w, out, stream=None) -> None:
+    act = _TORCH_ACT.get(p.act_dtype)
+    out_dt = torch.float32 if p.flags & MOE_FLAG_OUT_F32 else act
+    n = p.T * p.k
+    _check(_lib.moe_combine(ctypes.byref(p), _ptr(y, act, n * p.H, "y"),
+                            _ptr(pos, torch.int32, n, "pos"), _ptr(w, torch.float32, n, "w"),
+                            _ptr(out, out_dt, p.T * p.H, "out"), _stream(stream)), "moe_combine")

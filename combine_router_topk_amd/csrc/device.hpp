@@ -1,0 +1,144 @@
+// Device helpers shared by the routing kernels: 16-bit float conversions,
+// order-preserving integer keys for fp32 logits, and wave64 utilities.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxE = 1024;  // largest expert count the kernels size LDS for
+constexpr int kMaxR = 1024;  // largest virtual-rank count
+
+// ---- 16-bit activation formats --------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+// Hardware conversion in the default round-to-nearest-even mode.
+__device__ __forceinline__ uint32_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_to_f32(uint32_t bits16) {
+  if constexpr (ACT == 1) return f16_to_f32(bits16);
+  else return bf16_to_f32(bits16);
+}
+
+template <int ACT>
+__device__ __forceinline__ uint32_t f32_to_act(float f) {
+  if constexpr (ACT == 1) return f32_to_f16(f);
+  else return f32_to_bf16(f);
+}
+
+// 8 packed 16-bit values <-> 8 floats.
+template <int ACT>
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = act_to_f32<ACT>(w[i] & 0xffffu);
+    f[2 * i + 1] = act_to_f32<ACT>(w[i] >> 16);
+  }
+}
+
+template <int ACT>
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = f32_to_act<ACT>(f[2 * i]) | (f32_to_act<ACT>(f[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Pins a value as an fp32 register so the compiler cannot fold the
+// conversions around it into a mixed-precision FMA (which would round the
+// product directly to 16 bits and add +0.0, losing the sign of -0.0).
+__device__ __forceinline__ float keep_f32(float v) {
+  __asm__ volatile("" : "+v"(v));
+  return v;
+}
+
+// ---- order-preserving keys for top-k ---------------------------------------
+// Larger key = better logit. Finite values and +-inf map monotonically into
+// [0x007fffff, 0xff800000]; -0.0 is folded onto +0.0 so the two tie; any NaN
+// maps to 1 (below every number); 0 is reserved for "no candidate".
+
+__device__ __forceinline__ uint32_t logit_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;     // NaN
+  if ((u << 1) == 0u) u = 0u;                          // -0.0 -> +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_logit(uint32_t key) {
+  if (key == 1u) return __uint_as_float(0x7fc00000u);
+  const uint32_t u = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+  return __uint_as_float(u);
+}
+
+// ---- wave64 helpers --------------------------------------------------------
+
+__device__ __forceinline__ uint64_t ballot(bool pred) { return __ballot(pred); }
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Max over aligned groups of L lanes (L a power of two <= 64); every lane of
+// the group receives the result.
+template <int L>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+#pragma unroll
+  for (int off = L / 2; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Destination rank of expert e: its assigned replica if active, else its
+// primary copy, else the contiguous partition. Clamped so a bad table can
+// never index out of bounds.
+__device__ __forceinline__ int expert_rank(int e, int E, int R, const int* __restrict__ assign,
+                                           const int* __restrict__ rep, int maxrep) {
+  int r;
+  if (assign != nullptr && assign[e] >= 0) r = assign[e];
+  else if (rep != nullptr) r = rep[e * maxrep];
+  else r = e / (E / R);
+  return r < 0 ? 0 : (r >= R ? R - 1 : r);
+}
+
+}  // namespace moe

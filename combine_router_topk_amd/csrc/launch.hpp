@@ -1,0 +1,44 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+// Shapes are validated by the caller; these functions only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Token blocking used by the route and layout kernels. One function decides
+// it so the workspace size and the launches always agree.
+struct Blocking {
+  int route_tpb;    // tokens per route block
+  int route_nblk;   // route blocks
+  int layout_tpb;   // tokens per layout block
+  int layout_nblk;  // layout blocks
+};
+Blocking blocking_for(int T, int E);
+
+// Workspace bytes for route and layout (the larger of the two).
+size_t workspace_bytes(int T, int E, int R);
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                        int32_t* counts, int32_t* ws, hipStream_t s);
+
+hipError_t launch_assign(const int32_t* counts, int E, int R, const int32_t* rep, int maxrep,
+                         bool id_order, int32_t* assign, int32_t* active, hipStream_t s);
+
+hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const int32_t* assign,
+                         const int32_t* rep, int maxrep, int32_t* rank_of, int32_t* expert_offsets,
+                         int32_t* rank_offsets, int32_t* pos, int32_t* src, int32_t* dedup,
+                         int32_t* ws, hipStream_t s);
+
+hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T, int k, int H,
+                           hipStream_t s);
+
+hipError_t launch_standin(const void* send, const int32_t* src, const int32_t* idx, void* y, int T,
+                          int E, int k, int H, int act, hipStream_t s);
+
+hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, void* out, int T, int k,
+                          int H, int act, bool out_f32, hipStream_t s);
+
+}  // namespace moe

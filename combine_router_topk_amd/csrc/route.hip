@@ -1,0 +1,194 @@
+// Router top-k, gate weights and the global expert demand vector.
+//
+// "METRO AllGather vs AllToAll for MoE decode", section "METRO AllGather vs
+// AllToAll changes the routing information": every token's top-k is taken and
+// one demand count per expert is formed from all of them.
+//
+// Kernel 1 (route_topk): a group of L lanes owns one token's row of E logits
+// (V = E/L values per lane, coalesced loads). Each of the k rounds takes the
+// group maximum of order-preserving 32-bit keys with xor shuffles and then
+// the lowest expert id holding that key with ballots, so ties resolve to the
+// lower id without 64-bit shuffles. Lane j of the group keeps slot j; the
+// softmax over the selected logits is evaluated in fp64 by lanes 0..k-1 in
+// parallel and summed in ascending slot order. Selections are counted in an
+// LDS histogram per block, written as one row of a [blocks, E] matrix: no
+// global atomics.
+// Kernel 2 (column_sum): counts[e] = sum of column e of that matrix.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteTargetBlocks = 512;
+
+template <int L, int V>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int tpb, int32_t* __restrict__ idx,
+    float* __restrict__ w, int32_t* __restrict__ block_hist) {
+  extern __shared__ int s_hist[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_hist[e] = 0;
+  __syncthreads();
+
+  constexpr int TPW = kWave / L;  // tokens per wave step
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int grp = lane / L;
+  const int sl = lane % L;
+  const uint64_t gmask = (L == 64) ? ~0ull : ((1ull << L) - 1ull) << (grp * L);
+
+  const int t_begin = blockIdx.x * tpb;
+  const int t_end = min(T, t_begin + tpb);
+
+  for (int t0 = t_begin + wave * TPW; t0 < t_end; t0 += nwaves * TPW) {
+    const int t = t0 + grp;
+    const bool valid = t < t_end;
+    uint32_t key[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = sl + v * L;
+      key[v] = (valid && e < E) ? logit_key(logits[(size_t)t * E + e]) : 0u;
+    }
+
+    int my_e = 0;
+    uint32_t my_key = 0u, top_key = 0u;
+    for (int j = 0; j < k; ++j) {
+      uint32_t best = key[0];
+#pragma unroll
+      for (int v = 1; v < V; ++v) best = key[v] > best ? key[v] : best;
+      best = group_max<L>(best);
+      // lowest expert id e = v*L + lane-in-group whose key equals the maximum
+      int e_sel = 0;
+      bool found = false;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const uint64_t m = ballot(key[v] == best) & gmask;
+        if (!found && m != 0ull) {
+          e_sel = v * L + (__builtin_ctzll(m) - grp * L);
+          found = true;
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (v * L + sl == e_sel) key[v] = 0u;  // taken: never chosen again
+      if (sl == j) {
+        my_e = e_sel;
+        my_key = best;
+      }
+      if (j == 0) top_key = best;
+    }
+
+    // softmax over the k selected logits in fp64, lanes 0..k-1 of the group
+    double ex = 0.0;
+    if (sl < k) ex = exp(static_cast<double>(key_logit(my_key)) -
+                         static_cast<double>(key_logit(top_key)));
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += __shfl(ex, grp * L + j, kWave);
+    if (valid && sl < k) {
+      const size_t o = (size_t)t * k + sl;
+      idx[o] = my_e;
+      w[o] = static_cast<float>(ex / sum);
+      atomicAdd(&s_hist[my_e], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* row = block_hist + (size_t)blockIdx.x * E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) row[e] = s_hist[e];
+}
+
+// out[c] = sum over rows of M[rows, cols]; one block per 64 columns, the 16
+// waves split the rows and meet in LDS. Deterministic, no atomics.
+__global__ __launch_bounds__(1024) void column_sum_kernel(const int32_t* __restrict__ M, int rows,
+                                                          int cols, int32_t* __restrict__ out) {
+  __shared__ int part[16][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int c = blockIdx.x * kWave + lane;
+  int acc = 0;
+  if (c < cols) {
+    int r = wave;
+    for (; r + 48 < rows; r += 64) {
+      const int a = M[(size_t)r * cols + c], b = M[(size_t)(r + 16) * cols + c];
+      const int d = M[(size_t)(r + 32) * cols + c], f = M[(size_t)(r + 48) * cols + c];
+      acc += (a + b) + (d + f);
+    }
+    for (; r < rows; r += 16) acc += M[(size_t)r * cols + c];
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && c < cols) {
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += part[i][lane];
+    out[c] = s;
+  }
+}
+
+template <int L, int V>
+hipError_t launch_topk(const float* logits, int T, int E, int k, int tpb, int nblk, int32_t* idx,
+                       float* w, int32_t* ws, hipStream_t s) {
+  route_topk_kernel<L, V><<<nblk, kRouteThreads, E * sizeof(int), s>>>(logits, T, E, k, tpb, idx, w,
+                                                                       ws);
+  return hipGetLastError();
+}
+
+int lanes_per_token(int E) {
+  if (E <= 8) return 8;
+  if (E <= 16) return 16;
+  if (E <= 32) return 32;
+  return 64;
+}
+
+}  // namespace
+
+Blocking blocking_for(int T, int E) {
+  Blocking b{};
+  const int tpw = kWave / lanes_per_token(E);
+  const int step = tpw * (kRouteThreads / kWave);
+  int tpb = (T + kRouteTargetBlocks - 1) / kRouteTargetBlocks;
+  tpb = ((tpb + step - 1) / step) * step;
+  if (tpb < step) tpb = step;
+  b.route_tpb = tpb;
+  b.route_nblk = (T + tpb - 1) / tpb;
+  int ltpb = 64;
+  while ((T + ltpb - 1) / ltpb > 256) ltpb *= 2;
+  b.layout_tpb = ltpb;
+  b.layout_nblk = (T + ltpb - 1) / ltpb;
+  return b;
+}
+
+size_t workspace_bytes(int T, int E, int R) {
+  const Blocking b = blocking_for(T, E);
+  const size_t route = (size_t)b.route_nblk * E * sizeof(int32_t);
+  const size_t layout = (size_t)b.layout_nblk * (E + R) * sizeof(int32_t);
+  size_t n = route > layout ? route : layout;
+  n = (n + 255) & ~(size_t)255;
+  return n < 256 ? 256 : n;
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                        int32_t* counts, int32_t* ws, hipStream_t s) {
+  const Blocking b = blocking_for(T, E);
+  hipError_t err = hipSuccess;
+  if (T > 0) {
+    const int L = lanes_per_token(E);
+    const int tpb = b.route_tpb, n = b.route_nblk;
+    if (L == 8) err = launch_topk<8, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else if (L == 16) err = launch_topk<16, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else if (L == 32) err = launch_topk<32, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else if (E <= 64) err = launch_topk<64, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else if (E <= 128) err = launch_topk<64, 2>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else if (E <= 256) err = launch_topk<64, 4>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else if (E <= 512) err = launch_topk<64, 8>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else err = launch_topk<64, 16>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    if (err != hipSuccess) return err;
+  }
+  const int rows = T > 0 ? b.route_nblk : 0;
+  column_sum_kernel<<<(E + kWave - 1) / kWave, 1024, 0, s>>>(ws, rows, E, counts);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,95 @@
+"""The whole routing path on device buffers: route -> greedy replica
+assignment -> layout -> dispatch -> expert stand-in -> combine, each step one
+call into the HIP library. Torch provides the device memory and the stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import binding as B
+
+
+@dataclass
+class Buffers:
+    p: B.Problem
+    logits: torch.Tensor
+    x: torch.Tensor
+    rep: torch.Tensor | None
+    maxrep: int
+    ws: torch.Tensor
+    idx: torch.Tensor
+    w: torch.Tensor
+    counts: torch.Tensor
+    assign: torch.Tensor
+    active: torch.Tensor
+    rank_of: torch.Tensor
+    expert_offsets: torch.Tensor
+    rank_offsets: torch.Tensor
+    pos: torch.Tensor
+    src: torch.Tensor
+    dedup: torch.Tensor
+    send: torch.Tensor
+    y: torch.Tensor
+    out: torch.Tensor
+
+
+def allocate(p: B.Problem, logits: torch.Tensor, x: torch.Tensor, rep: torch.Tensor | None = None,
+             device: str | torch.device = "cuda") -> Buffers:
+    """Device buffers for one batch. `logits` [T, E] f32 and `x` [T, H] in the
+    activation dtype are copied to the device; `rep` is an int32 [E, maxrep]
+    replica table or None."""
+    dev = torch.device(device)
+    T, E, k, H, R = p.T, p.E, p.k, p.H, p.R
+    act = B._TORCH_ACT[p.act_dtype]
+    i32 = dict(dtype=torch.int32, device=dev)
+    out_dt = torch.float32 if p.flags & B.MOE_FLAG_OUT_F32 else act
+    rep_d = None if rep is None else rep.to(dev, torch.int32).contiguous()
+    maxrep = 1 if rep is None else int(rep.shape[1])
+    ws_bytes = B.moe_workspace_bytes(p)
+    return Buffers(
+        p=p, logits=logits.to(dev, torch.float32).contiguous(), x=x.to(dev).contiguous(),
+        rep=rep_d, maxrep=maxrep,
+        ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
+        idx=torch.empty(T * k, **i32), w=torch.empty(T * k, dtype=torch.float32, device=dev),
+        counts=torch.empty(E, **i32), assign=torch.empty(E, **i32), active=torch.empty(R, **i32),
+        rank_of=torch.empty(E, **i32), expert_offsets=torch.empty(E, **i32),
+        rank_offsets=torch.empty(R + 1, **i32), pos=torch.empty(T * k, **i32),
+        src=torch.empty(T * k, **i32), dedup=torch.empty(R, **i32),
+        send=torch.empty(T * k, H, dtype=act, device=dev),
+        y=torch.empty(T * k, H, dtype=act, device=dev),
+        out=torch.empty(T, H, dtype=out_dt, device=dev))
+
+
+def route(b: Buffers, stream=None) -> None:
+    B.moe_route(b.p, b.logits, b.idx, b.w, b.counts, b.ws, stream)
+
+
+def assign(b: Buffers, stream=None) -> None:
+    B.moe_assign_replicas(b.p, b.counts, b.rep, b.maxrep, b.assign, b.active, stream)
+
+
+def layout(b: Buffers, stream=None) -> None:
+    B.moe_layout(b.p, b.idx, b.assign, b.rep, b.maxrep, b.rank_of, b.expert_offsets,
+                 b.rank_offsets, b.pos, b.src, b.dedup, b.ws, stream)
+
+
+def dispatch(b: Buffers, stream=None) -> None:
+    B.moe_dispatch(b.p, b.x, b.pos, b.send, stream)
+
+
+def standin(b: Buffers, stream=None) -> None:
+    B.moe_expert_standin(b.p, b.send, b.src, b.idx, b.y, stream)
+
+
+def combine(b: Buffers, stream=None) -> None:
+    B.moe_combine(b.p, b.y, b.pos, b.w, b.out, stream)
+
+
+STEPS = (route, assign, layout, dispatch, standin, combine)
+
+
+def run(b: Buffers, stream=None) -> None:
+    for step in STEPS:
+        step(b, stream)

@@ -1,0 +1,191 @@
+/*
+ * moe_route.h -- C ABI of the single-GPU MoE token-routing path for AMD
+ * Instinct MI355X (gfx950): router top-k with gate weights, the expert demand
+ * vector, METRO-style greedy replica assignment, the rank-grouped dispatch
+ * layout with single-send dedup counts, the row dispatch, an expert stand-in,
+ * and the weighted combine.
+ *
+ * Sources (web pages on MoE dispatch and combine):
+ *   [METRO]  "METRO AllGather vs AllToAll for MoE decode" (fanout.sh).
+ *   [CORR]   News summary of "correlated expert placement and token
+ *            shuffling" for MoE pretraining (ainewsletter.today).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every array argument is a DEVICE pointer allocated and owned by the
+ *    caller. The library never allocates or frees device memory, never
+ *    synchronises, and only enqueues kernels on `stream` (a hipStream_t;
+ *    NULL means the null stream). Results are valid once the stream has
+ *    reached that point. Calls are stateless and may run concurrently on
+ *    different streams with different buffers.
+ *  - Every call returns a moe_status and never aborts. Host-side argument
+ *    checks happen before anything is enqueued: MOE_ERR_INVALID_ARG for a bad
+ *    shape, dtype, flag, a NULL pointer where data is needed, or a
+ *    misaligned pointer; MOE_ERR_WORKSPACE for a workspace smaller than
+ *    moe_workspace_bytes(). A failed kernel launch returns MOE_ERR_HIP.
+ *    moe_last_error() gives a one-line description of the last failure on
+ *    the calling thread.
+ *  - Data-dependent faults are not detected: expert ids in `idx` outside
+ *    [0, E), replica entries outside [-1, R), or `pos` / `src` values that
+ *    are not the permutation moe_layout wrote give an unspecified result,
+ *    but every kernel keeps its memory accesses inside the buffers the shape
+ *    describes (out-of-range entries are clamped or skipped).
+ *  - T = 0 is valid: per-token outputs are empty, per-expert and per-rank
+ *    outputs are written (zero counts, no active experts, zero offsets).
+ *  - Token activations are 16-bit floats (fp16 or bf16) in row-major [rows, H]
+ *    with H a multiple of 8, so each row is a whole number of 16-byte chunks;
+ *    activation pointers must be 16-byte aligned.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+/* Activation formats. */
+enum { MOE_F16 = 1, MOE_BF16 = 2 };
+
+/* Flags (bit set). */
+enum {
+  /* Greedy replica assignment visits active experts in ascending id instead
+   * of the default most-constrained-first order (fewest replicas, then id). */
+  MOE_FLAG_GREEDY_ID_ORDER = 1u << 0,
+  /* moe_combine writes fp32 rows instead of the activation format. */
+  MOE_FLAG_OUT_F32 = 1u << 1
+};
+
+/* Limits checked on the host. */
+enum { MOE_MAX_E = 1024, MOE_MAX_K = 16, MOE_MAX_R = 1024, MOE_MAX_REP = 16 };
+
+/* One routing problem.
+ *   T  tokens, T >= 0, T*k < 2^31
+ *   E  experts, 1 <= E <= 1024
+ *   k  experts selected per token, 1 <= k <= min(E, 16)
+ *   H  hidden width (elements per activation row), H > 0, H % 8 == 0
+ *   R  virtual expert-parallel ranks (= virtual GPUs), 1 <= R <= 1024; a
+ *      layout inside this GPU's memory, nothing is communicated
+ *   act_dtype  MOE_F16 or MOE_BF16
+ *   flags      MOE_FLAG_* bits                                               */
+typedef struct {
+  int32_t T, E, k, H, R;
+  int32_t act_dtype;
+  uint32_t flags;
+} moe_problem;
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+int32_t moe_version(void);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* moe_status_string(int32_t status);
+
+/* Description of the last non-OK status returned on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Bytes of device workspace moe_route and moe_layout need for this problem
+ * (one buffer of this size serves both; its contents need no initialisation
+ * and are not meaningful between calls). Host only; enqueues nothing. */
+moe_status moe_workspace_bytes(const moe_problem* p, size_t* bytes);
+
+/* Router top-k, gate weights and the global expert demand vector.
+ * [METRO] section "METRO AllGather vs AllToAll changes the routing
+ * information": top-k over every token, then one count per expert.
+ *   logits  f32 [T, E] row-major (read)
+ *   idx     i32 [T, k] (write): the k selected experts of each token, slot 0
+ *           the largest logit; ties go to the lower expert id, -0.0 ties
+ *           +0.0, a NaN logit ranks below every number
+ *   w       f32 [T, k] (write): softmax over the k selected logits, evaluated
+ *           in fp64 and rounded once to fp32 (the pages give no gate rule;
+ *           this is the reading taken)
+ *   counts  i32 [E] (write): number of (token, slot) pairs that chose e;
+ *           sums to T*k
+ *   ws      workspace of at least moe_workspace_bytes() bytes             */
+moe_status moe_route(const moe_problem* p, const float* logits, int32_t* idx, float* w,
+                     int32_t* counts, void* ws, size_t ws_bytes, void* stream);
+
+/* Greedy replica assignment: every active expert (counts[e] > 0) goes to one
+ * of its replicas, on the virtual GPU with the fewest experts activated so
+ * far; ties go to the lower GPU index. [METRO] sections "METRO AllGather vs
+ * AllToAll changes the routing information" and "Add the expert-weight
+ * traffic term" (greedy, not the optimal min-max assignment).
+ * Visiting order: most-constrained first (ascending number of replicas, then
+ * id) unless MOE_FLAG_GREEDY_ID_ORDER is set.
+ *   counts  i32 [E] (read)
+ *   rep     i32 [E, maxrep] (read) virtual GPU ids in [0, R) holding a copy of
+ *           each expert, -1 padded; rep[e][0] is the primary copy and must be
+ *           valid. NULL means no replicas: expert e lives on GPU e / (E / R)
+ *           (needs R | E).
+ *   maxrep  columns of rep, 1..16 (ignored when rep is NULL)
+ *   assign  i32 [E] (write): chosen GPU, or -1 for an inactive expert
+ *   active  i32 [R] (write): activated experts per virtual GPU              */
+moe_status moe_assign_replicas(const moe_problem* p, const int32_t* counts, const int32_t* rep,
+                               int32_t maxrep, int32_t* assign, int32_t* active, void* stream);
+
+/* Dispatch layout and single-send dedup counts.
+ * [METRO] section "Work the 8-GPU payload example" (an all-to-all sends one
+ * chunk per destination rank) and section "Distinguish METRO from backend
+ * names" (variable-size all-to-all driven by destination counts); [CORR]
+ * section "Two locality techniques" (a token is sent to a GPU at most once).
+ * The send buffer has exactly T*k rows, grouped by destination rank, inside a
+ * rank by expert id, inside an expert by token (stable).
+ *   idx      i32 [T, k] (read), as written by moe_route
+ *   assign   i32 [E] or NULL (read): destination of active experts; inactive
+ *            experts (-1) and the NULL case use the primary copy
+ *   rep, maxrep  as in moe_assign_replicas (NULL: contiguous partition)
+ *   rank_of         i32 [E]   (write) destination rank of each expert
+ *   expert_offsets  i32 [E]   (write) first send row of expert e's segment
+ *   rank_offsets    i32 [R+1] (write) first send row of each rank; [R] = T*k
+ *   pos   i32 [T*k] (write) send row of pair (t, j) at index t*k + j
+ *   src   i32 [T*k] (write) inverse of pos: flat (t, j) index of each row
+ *   dedup i32 [R]   (write) tokens with at least one expert on rank r: the
+ *                   rows a single-send dispatcher sends to r               */
+moe_status moe_layout(const moe_problem* p, const int32_t* idx, const int32_t* assign,
+                      const int32_t* rep, int32_t maxrep, int32_t* rank_of,
+                      int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos,
+                      int32_t* src, int32_t* dedup, void* ws, size_t ws_bytes, void* stream);
+
+/* Row dispatch: send[pos[i]] = x[i / k] for every i < T*k, a bit copy.
+ * [METRO] section "Work the 8-GPU payload example" (the dispatch payload is
+ * token activation rows).
+ *   x     16-bit [T, H] (read)    pos  i32 [T*k] (read)
+ *   send  16-bit [T*k, H] (write); must not overlap x                       */
+moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* pos, void* send,
+                        void* stream);
+
+/* Expert stand-in (the pages' expert GEMMs need trained weights): for send
+ * row r routed to expert e = idx[src[r]], y[r] = round16(fp32(send[r]) * s)
+ * with s = 1 + e/E, s and the product each rounded to fp32, round16 to
+ * nearest-even in the activation format.
+ *   send 16-bit [T*k, H] (read)  src i32 [T*k]  idx i32 [T, k]
+ *   y    16-bit [T*k, H] (write); may alias send                           */
+moe_status moe_expert_standin(const moe_problem* p, const void* send, const int32_t* src,
+                              const int32_t* idx, void* y, void* stream);
+
+/* Weighted combine back to token order:
+ * out[t] = sum over j = 0..k-1 (ascending) of w[t, j] * y[pos[t*k + j]],
+ * accumulated in fp32, written in the activation format (round to
+ * nearest-even) or as fp32 with MOE_FLAG_OUT_F32.
+ * [METRO] section "METRO AllGather vs AllToAll changes the routing
+ * information" (expert outputs return through a combine); [CORR] section
+ * "Why communication is the target".
+ *   y    16-bit [T*k, H] (read)  pos i32 [T*k]  w f32 [T, k]
+ *   out  [T, H] in the activation format or fp32 (write); must not overlap y */
+moe_status moe_combine(const moe_problem* p, const void* y, const int32_t* pos, const float* w,
+                       void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

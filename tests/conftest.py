@@ -8,6 +8,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
+LIB = os.path.join(ROOT, "combine_router_topk_amd", "libmoe_route.so")
+
+# Tests load what is built; they build only when nothing is.
+if not os.path.exists(LIB):
+    from combine_router_topk_amd.build import build as _build
+    _build()
 
 
 def pytest_configure(config):

@@ -1,0 +1,108 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI on
+seeded inputs and compare every output with the CPU oracle.
+
+Bars: bit-exact for every index, count, offset and row output; gate weights
+within rtol 1e-6; the combine within |out - ref| <= 1e-3 + 4e-3 |ref| for the
+16-bit output (ref = the oracle's fp64 sum) and within the fp32 accumulation
+bound k * 2^-24 * sum_j |w_j y_j| for the fp32 output.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from combine_router_topk_amd import binding as B
+from combine_router_topk_amd import path as P
+
+W_RTOL = 1e-6
+OUT_RTOL, OUT_ATOL = 4e-3, 1e-3
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_act(act: int):
+    return torch.float16 if act == synth.F16 else torch.bfloat16
+
+
+def bits_to_tensor(bits: np.ndarray, act: int) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch_act(act))
+
+
+def tensor_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def run_gpu(w: synth.Workload, logits: np.ndarray, x: np.ndarray, rep: np.ndarray | None,
+            flags: int = 0, inplace_standin: bool = False) -> P.Buffers:
+    p = B.make_problem(w.T, w.E, w.k, w.H, w.R, w.act_dtype, flags)
+    b = P.allocate(p, torch.from_numpy(logits), bits_to_tensor(x, w.act_dtype),
+                   None if rep is None else torch.from_numpy(rep))
+    if inplace_standin:
+        b.y = b.send
+    P.run(b)
+    torch.cuda.synchronize()
+    return b
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+META_KEYS = ("counts", "assign", "active", "rank_of", "expert_offsets", "rank_offsets", "pos",
+             "src", "dedup")
+
+
+def check_meta(b: P.Buffers, ref: dict, T: int, k: int) -> None:
+    assert np.array_equal(host(b.idx).reshape(T, k), ref["idx"]), "idx"
+    for key in META_KEYS:
+        got = host(getattr(b, key))
+        assert np.array_equal(got, ref[key]), (key, got[:16], ref[key][:16])
+    wg = host(b.w).reshape(T, k).astype(np.float64)
+    wr = ref["w"].astype(np.float64)
+    assert np.array_equal(np.isnan(wg), np.isnan(wr)), "w NaN pattern"
+    bad = np.abs(wg - wr) > W_RTOL * np.abs(wr)
+    assert not bad.any(), ("w", np.argwhere(bad)[:5], wg[bad][:5], wr[bad][:5])
+
+
+def check_rows(b: P.Buffers, ref: dict, x: np.ndarray, w: synth.Workload,
+               send_rows: np.ndarray | None, tokens: np.ndarray | None, out_f32: bool,
+               check_send: bool = True) -> None:
+    r = oracle.rows_for(ref, x, w.E, w.k, w.act_dtype, send_rows=send_rows, tokens=tokens)
+    rows_t = torch.from_numpy(r["send_rows"]).to(b.send.device, torch.int64)
+    if check_send:
+        got_send = tensor_bits(b.send.index_select(0, rows_t))
+        assert np.array_equal(got_send, r["send"]), "send rows"
+    got_y = tensor_bits(b.y.index_select(0, rows_t))
+    if not np.array_equal(got_y, r["y"]):
+        bad = np.argwhere(got_y != r["y"])[:8]
+        flat = ref["idx"].ravel()
+        detail = [(int(r["send_rows"][i]), int(c), hex(int(r["send"][i, c])),
+                   int(flat[ref["src"][r["send_rows"][i]]]), hex(int(got_y[i, c])), hex(int(r["y"][i, c])))
+                  for i, c in bad]
+        raise AssertionError(f"y rows: {int((got_y != r['y']).sum())} mismatches; "
+                             f"(row, col, send bits, expert, got, want): {detail}")
+    tok_t = torch.from_numpy(r["tokens"]).to(b.out.device, torch.int64)
+    got = b.out.index_select(0, tok_t).float().cpu().numpy().astype(np.float64)
+    refo = r["out"]
+    if out_f32:
+        # fp32 accumulation bound: k roundings of at most 2^-24 of the running sum
+        mag = np.zeros_like(refo)
+        toks = r["tokens"]
+        for j in range(w.k):
+            rows = ref["pos"][toks * w.k + j]
+            yrow = oracle.decode16(oracle.expert_standin(
+                oracle.dispatch_rows(x, ref["src"], w.k, rows), ref["idx"].ravel()[ref["src"][rows]],
+                w.E, w.act_dtype), w.act_dtype).astype(np.float64)
+            mag += np.abs(ref["w"][toks, j].astype(np.float64))[:, None] * np.abs(yrow)
+        bound = w.k * 2.0 ** -24 * mag + 1e-30
+        bad = np.abs(got - refo) > bound
+    else:
+        bad = np.abs(got - refo) > OUT_ATOL + OUT_RTOL * np.abs(refo)
+    assert not bad.any(), ("out", np.argwhere(bad)[:5], got[bad][:5], refo[bad][:5])

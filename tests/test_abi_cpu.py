@@ -1,0 +1,97 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/moe_route.h declares, and its host-side checks turn bad arguments
+into status codes before anything is enqueued (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from combine_router_topk_amd import binding as B
+
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_and_library_exports_every_entry_point():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED), names
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert B.moe_version() >= 10000
+    assert B.moe_status_string(0) == "ok"
+    assert B.moe_status_string(3) == "workspace too small"
+    assert B.moe_status_string(99) == "unknown status"
+
+
+def prob(**kw):
+    d = dict(T=256, E=8, k=2, H=128, R=4, act_dtype=B.MOE_F16, flags=0)
+    d.update(kw)
+    return B.make_problem(d["T"], d["E"], d["k"], d["H"], d["R"], d["act_dtype"], d["flags"])
+
+
+@pytest.mark.parametrize("bad", [dict(T=-1), dict(E=0), dict(E=1025), dict(k=0), dict(k=9),
+                                 dict(E=32, k=17), dict(H=12), dict(H=0), dict(R=0),
+                                 dict(R=1025), dict(act_dtype=3), dict(flags=1 << 7),
+                                 dict(T=1 << 30, k=4)])
+def test_invalid_problems_rejected(bad):
+    n = ctypes.c_size_t(0)
+    st = B._lib.moe_workspace_bytes(ctypes.byref(prob(**bad)), ctypes.byref(n))
+    assert st == B.MOE_ERR_INVALID_ARG, (bad, B.moe_last_error())
+    assert B.moe_last_error()
+
+
+def test_workspace_size_grows_with_tokens():
+    sizes = [B.moe_workspace_bytes(prob(T=t, E=64, R=32)) for t in (0, 1, 1000, 16384, 65536)]
+    assert all(s % 256 == 0 and s > 0 for s in sizes)
+    assert sizes == sorted(sizes)
+
+
+def test_null_pointers_rejected_before_any_launch():
+    p = prob()
+    ref = ctypes.byref(p)
+    lib = B._lib
+    fake = ctypes.c_void_p(1 << 20)           # aligned, never dereferenced
+    mis = ctypes.c_void_p((1 << 20) + 4)      # 4-byte aligned, not 16
+    assert lib.moe_route(ref, None, fake, fake, fake, fake, 1 << 20, None) == B.MOE_ERR_INVALID_ARG
+    assert "logits" in B.moe_last_error()
+    assert lib.moe_route(ref, fake, fake, fake, fake, fake, 16, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_assign_replicas(ref, fake, None, 1, None, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_assign_replicas(ref, fake, fake, 0, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_layout(ref, fake, None, None, 1, fake, fake, fake, None, fake, fake, fake,
+                          1 << 20, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(ref, mis, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert "aligned" in B.moe_last_error()
+    assert lib.moe_expert_standin(ref, fake, fake, fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ref, fake, fake, None, fake, None) == B.MOE_ERR_INVALID_ARG
+    # no replica table: R must divide E
+    p2 = prob(E=12, R=5)
+    assert lib.moe_assign_replicas(ctypes.byref(p2), fake, None, 1, fake, fake, None) \
+        == B.MOE_ERR_INVALID_ARG
+
+
+def test_empty_rows_are_noops():
+    p = prob(T=0)
+    ref = ctypes.byref(p)
+    assert B._lib.moe_dispatch(ref, None, None, None, None) == B.MOE_OK
+    assert B._lib.moe_expert_standin(ref, None, None, None, None, None) == B.MOE_OK
+    assert B._lib.moe_combine(ref, None, None, None, None, None) == B.MOE_OK
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "combine_router_topk_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", text), f

@@ -1,0 +1,150 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on seeded synthetic inputs (every index/count/offset/row output bit-exact,
+gate weights within rtol 1e-6, combine within rtol 4e-3 / atol 1e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from combine_router_topk_amd import binding as B
+from pathcheck import check_meta, check_rows, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+# Reduced shapes: same routing structure, sizes the oracle finishes in
+# seconds, several route/layout blocks and a ragged tail in tokens and in
+# 16-byte row chunks.
+SMALL = [
+    synth.TINY,
+    synth.DECODE,
+    synth.scaled(synth.TRAIN_TOP2, T=3001, H=512),
+    synth.scaled(synth.TRAIN_TOP6, T=2053, H=264),
+    synth.scaled(synth.LARGE, T=777, H=7168),
+]
+
+
+def run_and_check(w, seed=0, flags=0, rep="table", order="constrained", logits=None, x=None,
+                  send_rows=None, tokens=None, inplace=False):
+    say(f"[case] {w.name} seed={seed} flags={flags} inplace={inplace}")
+    logits = synth.make_logits(w, seed) if logits is None else logits
+    x = synth.make_x(w, seed) if x is None else x
+    rep = synth.replica_table(w) if isinstance(rep, str) else rep
+    ref = oracle.route_and_layout(w.T, w.E, w.k, w.R, logits, rep, order)
+    b = run_gpu(w, logits, x, rep, flags, inplace_standin=inplace)
+    check_meta(b, ref, w.T, w.k)
+    check_rows(b, ref, x, w, send_rows, tokens, out_f32=bool(flags & B.MOE_FLAG_OUT_F32),
+               check_send=not inplace)
+    return b, ref
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_workloads_all_outputs(w, seed):
+    run_and_check(w, seed)
+
+
+def test_decode_greedy_id_order():
+    w = synth.DECODE
+    b, ref = run_and_check(w, 0, flags=B.MOE_FLAG_GREEDY_ID_ORDER, order="id")
+    assert ref["active"].max() >= 32
+
+
+@pytest.mark.parametrize("w", [synth.TINY, synth.scaled(synth.TRAIN_TOP6, T=999, H=128),
+                               synth.scaled(synth.LARGE, T=300, H=1024)], ids=lambda w: w.name)
+def test_fp32_output_accumulation_bound(w):
+    run_and_check(w, 1, flags=B.MOE_FLAG_OUT_F32)
+
+
+def test_inplace_standin():
+    run_and_check(synth.scaled(synth.TRAIN_TOP2, T=1000, H=256), 2, inplace=True)
+
+
+def test_deterministic_bitwise():
+    w = synth.scaled(synth.TRAIN_TOP6, T=4000, H=64)
+    l, x = synth.make_logits(w, 3), synth.make_x(w, 3)
+    a = run_gpu(w, l, x, None)
+    b = run_gpu(w, l, x, None)
+    for key in ("idx", "w", "counts", "pos", "src", "dedup", "send", "y", "out"):
+        assert torch.equal(getattr(a, key).view(torch.int8) if getattr(a, key).dtype.is_floating_point
+                           else getattr(a, key),
+                           getattr(b, key).view(torch.int8) if getattr(b, key).dtype.is_floating_point
+                           else getattr(b, key)), key
+
+
+# ---- shapes at the edges of the kernels' blocking --------------------------
+
+EDGE = [
+    ("E1_k1_R1_H8", 1, 1, 1, 1, 8),
+    ("E5_k3_R5", 97, 5, 3, 5, 24),          # 8 lanes per token, padding lanes
+    ("E8_k8_fullsort", 300, 8, 8, 2, 16),   # k = E
+    ("E12_k5_R3", 513, 12, 5, 3, 40),       # 16 lanes, scale 1 + e/12 not exact
+    ("E20_k4_R4", 257, 20, 4, 4, 8),        # 32 lanes
+    ("E100_k7_R10", 611, 100, 7, 10, 72),   # 2 values per lane, padded
+    ("E1024_k16_R1024", 300, 1024, 16, 1024, 16),  # largest E, k and R
+    ("T1", 1, 64, 2, 32, 4096),
+]
+
+
+@pytest.mark.parametrize("name,T,E,k,R,H", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_shapes(name, T, E, k, R, H):
+    w = synth.Workload(name, T, E, k, H, R, synth.BF16, "none", False)
+    run_and_check(w, 5)
+
+
+def test_ties_signed_zeros_nan_inf():
+    rng = np.random.default_rng(7)
+    T, E, k, R = 700, 16, 5, 4
+    l = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    l[rng.random((T, E)) < 0.2] = -0.0
+    l[rng.random((T, E)) < 0.05] = np.nan
+    l[rng.random((T, E)) < 0.02] = np.inf
+    l[rng.random((T, E)) < 0.02] = -np.inf
+    w = synth.Workload("ties", T, E, k, 64, R, synth.F16, "none", False)
+    x = synth.make_x(w, 0)
+    say(f"[case] ties T={T} E={E} k={k}")
+    ref = oracle.route_and_layout(T, E, k, R, l)
+    b = run_gpu(w, l, x, None)
+    check_meta(b, ref, T, k)
+
+
+@pytest.mark.parametrize("order", ["constrained", "id"])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_replica_tables(order, seed):
+    rng = np.random.default_rng(100 + seed)
+    E, R, maxrep = 64, 8, 3
+    rep = np.full((E, maxrep), -1, np.int32)
+    for e in range(E):
+        n = int(rng.integers(1, maxrep + 1))
+        rep[e, :n] = rng.choice(R, size=n, replace=False)
+    w = synth.Workload(f"rep{seed}", 500, E, 4, 64, R, synth.BF16, "zipf1.2", False)
+    flags = B.MOE_FLAG_GREEDY_ID_ORDER if order == "id" else 0
+    run_and_check(w, seed, flags=flags, rep=rep, order=order)
+
+
+def test_empty_batch():
+    w = synth.Workload("empty", 0, 8, 2, 128, 4, synth.F16, "none", False)
+    say("[case] empty batch")
+    b = run_gpu(w, np.zeros((0, 8), np.float32), np.zeros((0, 128), np.uint16), None)
+    assert b.counts.cpu().tolist() == [0] * 8
+    assert b.assign.cpu().tolist() == [-1] * 8
+    assert b.active.cpu().tolist() == [0] * 4
+    assert b.rank_offsets.cpu().tolist() == [0] * 5
+    assert b.expert_offsets.cpu().tolist() == [0] * 8
+    assert b.dedup.cpu().tolist() == [0] * 4
+
+
+def test_binding_rejects_short_buffers_and_workspace():
+    w = synth.TINY
+    p = B.make_problem(w.T, w.E, w.k, w.H, w.R, w.act_dtype)
+    dev = torch.device("cuda")
+    logits = torch.zeros(w.T, w.E, device=dev)
+    idx = torch.empty(w.T * w.k, dtype=torch.int32, device=dev)
+    wt = torch.empty(w.T * w.k, device=dev)
+    counts = torch.empty(w.E, dtype=torch.int32, device=dev)
+    small_ws = torch.empty(64, dtype=torch.uint8, device=dev)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(p, logits, idx, wt, counts, small_ws)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE
+    with pytest.raises(ValueError):
+        B.moe_route(p, logits, idx[:10], wt, counts, small_ws)
