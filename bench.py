@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "dispatch+combine HBM GB/s (% of peak) and routed rows/s at T=16384,E=64,top-2"
 PEAK_GBPS = 8000.0          # MI355X HBM3E peak
 DEFAULT_WORKLOAD = "train_T16384_E64_k2_H4096_bf16_clustered"
-PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+PROFILE_MD = os.path.join(ROOT, "profiles", "dispatch_combine_T16384_E64_k2_H4096_bf16.md")
 FLUSH_BYTES = 1 << 30
 
 
@@ -57,9 +57,10 @@ def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 PMC counters, if the
     counters were taken on the current kernel source for this workload."""
     try:
-        with open(PMC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+        with open(PROFILE_MD) as f:
+            line = next(l for l in f if l.startswith("traffic-json: "))
+        rec = json.loads(line[len("traffic-json: "):])
+    except (OSError, ValueError, StopIteration):
         return None
     if rec.get("rows_hip_sha") != kernel_source_digest() or rec.get("workload") != workload:
         return None
