@@ -10,6 +10,7 @@ namespace moe {
 constexpr int kWave = 64;
 constexpr int kMaxE = 1024;  // largest expert count the kernels size LDS for
 constexpr int kMaxR = 1024;  // largest virtual-rank count
+constexpr int kMaxK = 16;    // largest number of experts per token
 
 // ---- 16-bit activation formats --------------------------------------------
 
@@ -101,16 +102,76 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Max over aligned groups of L lanes (L a power of two <= 64); every lane of
-// the group receives the result.
+// ---- DPP lane exchanges (gfx9 encodings) ----------------------------------
+// Each is a VALU modifier, not an LDS round trip.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+
+// Max over aligned groups of L lanes (L in {8, 16, 32, 64}); every lane of the
+// group receives the result. Butterfly within rows of 16 lanes, then the row
+// maxima are read into scalar registers for groups wider than a row.
 template <int L>
 __device__ __forceinline__ uint32_t group_max(uint32_t v) {
-#pragma unroll
-  for (int off = L / 2; off > 0; off >>= 1) {
-    const uint32_t o = __shfl_xor(v, off, kWave);
-    v = o > v ? o : v;
+  v = umax(v, dpp<kDppXor1>(v));
+  v = umax(v, dpp<kDppXor2>(v));
+  v = umax(v, dpp<kDppHalfMirror>(v));
+  if constexpr (L >= 16) v = umax(v, dpp<kDppMirror>(v));
+  if constexpr (L == 32) {
+    const uint32_t g0 = umax(readlane(v, 0), readlane(v, 16));
+    const uint32_t g1 = umax(readlane(v, 32), readlane(v, 48));
+    v = (__lane_id() < 32) ? g0 : g1;
+  } else if constexpr (L == 64) {
+    v = umax(umax(readlane(v, 0), readlane(v, 16)), umax(readlane(v, 32), readlane(v, 48)));
   }
   return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint64_t lo = dpp<CTRL>(static_cast<uint32_t>(u));
+  const uint64_t hi = dpp<CTRL>(static_cast<uint32_t>(u >> 32));
+  return __longlong_as_double(static_cast<long long>(lo | (hi << 32)));
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint64_t lo = readlane(static_cast<uint32_t>(u), lane);
+  const uint64_t hi = readlane(static_cast<uint32_t>(u >> 32), lane);
+  return __longlong_as_double(static_cast<long long>(lo | (hi << 32)));
+}
+
+// Sum over the first min(L, 16) lanes of each aligned group of L lanes (the
+// other lanes of a group must hold 0, or be ignored by the caller when
+// L <= 16); every lane of the group receives it. Fixed tree order, so the
+// result is deterministic.
+template <int L>
+__device__ __forceinline__ double group_sum16_f64(double x) {
+  x += dpp_f64<kDppXor1>(x);
+  x += dpp_f64<kDppXor2>(x);
+  x += dpp_f64<kDppHalfMirror>(x);
+  if constexpr (L >= 16) x += dpp_f64<kDppMirror>(x);
+  if constexpr (L == 32) {
+    const double g0 = readlane_f64(x, 0), g1 = readlane_f64(x, 32);
+    x = (__lane_id() < 32) ? g0 : g1;
+  } else if constexpr (L == 64) {
+    x = readlane_f64(x, 0);
+  }
+  return x;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -11,12 +11,12 @@ namespace moe {
 // Token blocking used by the route and layout kernels. One function decides
 // it so the workspace size and the launches always agree.
 struct Blocking {
-  int route_tpb;    // tokens per route block
-  int route_nblk;   // route blocks
-  int layout_tpb;   // tokens per layout block
-  int layout_nblk;  // layout blocks
+  int route_tpb;          // tokens per route block
+  int route_nblk;         // route blocks (<= 512)
+  int layout_tpb;         // tokens per layout block
+  int layout_nblk;        // layout blocks (<= 32 * waves per column task, <= 256)
 };
-Blocking blocking_for(int T, int E);
+Blocking blocking_for(int T, int E, int R);
 
 // Workspace bytes for route and layout (the larger of the two).
 size_t workspace_bytes(int T, int E, int R);

@@ -16,9 +16,12 @@
 //  1. layout_count: per block of tokens, an LDS histogram of the selected
 //     experts and of the distinct destination ranks per token (dedup), each
 //     written as one row of a [blocks, E] / [blocks, R] matrix.
-//  2. layout_plan (one workgroup): rank of every expert; per-expert totals and
-//     the exclusive scan of the expert histogram over blocks (in place);
-//     expert and rank offsets in (rank, expert) order; dedup totals.
+//  2. layout_plan (one workgroup): one pass over both matrices, every wave
+//     loading its whole row segment in one batch: per-expert totals and the
+//     exclusive scan of the expert histogram over blocks (in place), dedup
+//     totals. Then the rank of every expert, per-rank row totals (LDS adds)
+//     and their block scan give the rank offsets; an expert's offset is its
+//     rank's offset plus the rows of lower-id experts on the same rank.
 //  3. layout_permute: per block, the stable rank of each pair among the
 //     block's pairs with the same expert: inside a wave by matching expert
 //     ids with one ballot per id bit and counting lower lanes; across the
@@ -31,10 +34,10 @@ namespace moe {
 
 namespace {
 
-constexpr int kCountThreads = 256;
+constexpr int kCountThreads = 1024;
 constexpr int kPlanThreads = 1024;
-constexpr int kPermThreads = 256;
-constexpr int kPermWaves = kPermThreads / kWave;
+constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kSegRegs = 48;  // rows per wave segment in the plan's column pass
 
 __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
@@ -59,12 +62,18 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
   for (size_t i = i0 + threadIdx.x; i < i1; i += blockDim.x)
     atomicAdd(&s_hist[clamp_expert(idx[i], E)], 1);
   for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
+    // ranks of the token's k experts in registers, then one count per
+    // distinct rank (the first slot that reaches it)
     const int32_t* row = idx + (size_t)t * k;
-    for (int j = 0; j < k; ++j) {
-      const int r = s_rank[clamp_expert(row[j], E)];
+    int rk[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) rk[j] = j < k ? s_rank[clamp_expert(row[j], E)] : -1 - j;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
       bool seen = false;
-      for (int jj = 0; jj < j; ++jj) seen |= (s_rank[clamp_expert(row[jj], E)] == r);
-      if (!seen) atomicAdd(&s_ded[r], 1);
+#pragma unroll
+      for (int jj = 0; jj < j; ++jj) seen |= (rk[jj] == rk[j]);
+      if (j < k && !seen) atomicAdd(&s_ded[rk[j]], 1);
     }
   }
   __syncthreads();
@@ -72,38 +81,60 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
   for (int r = threadIdx.x; r < R; r += blockDim.x) ded[(size_t)blockIdx.x * R + r] = s_ded[r];
 }
 
-// Column totals of M[rows, cols] into tot[] (LDS); with `scan`, M is replaced
-// by its exclusive prefix over rows, column by column. 16 waves split the rows
-// into segments; lanes are columns (64 at a time).
-__device__ void column_scan(int32_t* __restrict__ M, int rows, int cols, bool scan, int* tot,
-                            int (*part)[kWave]) {
+// Column pass over the two per-block matrices: hist [rows, E] is replaced by
+// its exclusive prefix over rows (column by column) and its column totals go
+// to s_cnt; ded [rows, R] is only summed into s_ded. The work is cut into
+// tasks of 64 columns; the 16 waves are shared among as many tasks as fit,
+// each task's waves splitting the rows into segments of at most kSegRegs
+// rows (the layout blocking guarantees it), loaded in one batch and kept in
+// registers: one memory round trip per group of tasks.
+__device__ void column_pass(int32_t* __restrict__ hist, int E, const int32_t* __restrict__ ded, int R,
+                            int rows, int* s_cnt, int* s_ded, int (*part)[kWave]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int nw = kPlanThreads / kWave;
-  const int seg = (rows + nw - 1) / nw;
-  const int r_lo = min(rows, wave * seg), r_hi = min(rows, r_lo + seg);
-  for (int c0 = 0; c0 < cols; c0 += kWave) {
-    const int c = c0 + lane;
+  const int ch_h = (E + kWave - 1) / kWave;
+  const int tasks = ch_h + (R + kWave - 1) / kWave;
+  const int S = tasks >= kPlanWaves ? 1 : kPlanWaves / tasks;  // waves per task
+  const int G = kPlanWaves / S;                                 // tasks per group
+  const int seg = (rows + S - 1) / S;
+  const int sw = wave % S;
+  const int r_lo = min(rows, sw * seg), r_hi = min(rows, r_lo + seg);
+  for (int g0 = 0; g0 < tasks; g0 += G) {
+    const int task = g0 + wave / S;
+    const bool on = (wave / S) < G && task < tasks;
+    const bool is_h = task < ch_h;
+    const int cols = is_h ? E : R;
+    const int c = (is_h ? task : task - ch_h) * kWave + lane;
+    const bool col_ok = on && c < cols;
+    const int32_t* M = is_h ? hist : ded;
+    int v[kSegRegs];
     int s = 0;
-    if (c < cols)
-      for (int r = r_lo; r < r_hi; ++r) s += M[(size_t)r * cols + c];
+#pragma unroll
+    for (int i = 0; i < kSegRegs; ++i) {
+      const int r = r_lo + i;
+      v[i] = (col_ok && r < r_hi) ? M[(size_t)r * cols + c] : 0;
+      s += v[i];
+    }
     part[wave][lane] = s;
     __syncthreads();
     int pre = 0, all = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int v = part[w][lane];
-      pre += (w < wave) ? v : 0;
-      all += v;
+    if (on) {  // waves past the last task of the group own no rows of part[]
+      const int w0 = (wave / S) * S;
+      for (int i = 0; i < S; ++i) {
+        const int x = part[w0 + i][lane];
+        pre += (i < sw) ? x : 0;
+        all += x;
+      }
     }
-    if (c < cols) {
-      if (wave == 0) tot[c] = all;
-      if (scan) {
+    if (col_ok) {
+      if (sw == 0) (is_h ? s_cnt : s_ded)[c] = all;
+      if (is_h) {
         int run = pre;
-        for (int r = r_lo; r < r_hi; ++r) {
-          const size_t o = (size_t)r * cols + c;
-          const int v = M[o];
-          M[o] = run;
-          run += v;
+#pragma unroll
+        for (int i = 0; i < kSegRegs; ++i) {
+          const int r = r_lo + i;
+          if (r < r_hi) hist[(size_t)r * cols + c] = run;
+          run += v[i];
         }
       }
     }
@@ -111,54 +142,101 @@ __device__ void column_scan(int32_t* __restrict__ M, int rows, int cols, bool sc
   }
 }
 
+// Exclusive prefix sum of one value per thread over the whole block (1024
+// threads); returns the prefix and writes the block total to *total.
+__device__ int block_excl_scan(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int incl = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) s_wave[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) {
+    const int x = s_wave[w];
+    before += (w < wave) ? x : 0;
+    all += x;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void layout_plan_kernel(
     int T, int E, int k, int R, int nblk, int32_t* __restrict__ hist, const int32_t* __restrict__ ded,
     const int32_t* __restrict__ assign, const int32_t* __restrict__ rep, int maxrep,
     int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ dedup) {
-  __shared__ int s_rank[kMaxE];
-  __shared__ int s_cnt[kMaxE];
+  __shared__ __align__(16) int s_rank[kMaxE + 8];
+  __shared__ __align__(16) int s_cnt[kMaxE + 8];
   __shared__ int s_ded[kMaxR];
-  __shared__ int part[kPlanThreads / kWave][kWave];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += blockDim.x) {
-    const int r = expert_rank(e, E, R, assign, rep, maxrep);
-    s_rank[e] = r;
-    rank_of[e] = r;
+  __shared__ int s_rtok[kMaxR];
+  __shared__ int s_roff[kMaxR];
+  __shared__ int part[kPlanWaves][kWave];
+  __shared__ int s_wave[kPlanWaves];
+  const int tid = threadIdx.x;  // E, R <= 1024 == blockDim.x: one expert / rank per thread
+  // issue the expert-rank loads now, use them after the column pass
+  int a_e = -1, p_e = 0;
+  if (tid < E) {
+    if (assign != nullptr) a_e = assign[tid];
+    p_e = rep != nullptr ? rep[tid * maxrep] : tid / (E / R);
   }
-  column_scan(hist, nblk, E, true, s_cnt, part);
-  column_scan(const_cast<int32_t*>(ded), nblk, R, false, s_ded, part);
+  if (tid < R) s_rtok[tid] = 0;
+  column_pass(hist, E, ded, R, nblk, s_cnt, s_ded, part);  // ends with a barrier
+
+  int my_r = 0;
+  if (tid < E) {
+    my_r = a_e >= 0 ? a_e : p_e;
+    my_r = my_r < 0 ? 0 : (my_r >= R ? R - 1 : my_r);
+    s_rank[tid] = my_r;
+    rank_of[tid] = my_r;
+    atomicAdd(&s_rtok[my_r], s_cnt[tid]);
+  } else if (tid < ((E + 7) & ~7)) {
+    s_rank[tid] = 0x7fffffff;  // padding never matches a rank
+    s_cnt[tid] = 0;
+  }
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) {
-    const int r = s_rank[e];
+  int total = 0;
+  const int roff = block_excl_scan(tid < R ? s_rtok[tid] : 0, s_wave, &total);
+  if (tid < R) {
+    s_roff[tid] = roff;
+    rank_offsets[tid] = roff;
+    dedup[tid] = s_ded[tid];
+  }
+  if (tid == 0) rank_offsets[R] = total;
+  __syncthreads();
+  if (tid < E) {
+    // rows of lower-id experts on the same rank, 8 LDS entries per step
     int acc = 0;
-    for (int e2 = 0; e2 < E; ++e2) {
-      const int r2 = s_rank[e2];
-      acc += (r2 < r || (r2 == r && e2 < e)) ? s_cnt[e2] : 0;
+    const int e_pad = (E + 7) & ~7;
+    for (int b = 0; b < e_pad; b += 8) {
+      const int4 r0 = *reinterpret_cast<const int4*>(&s_rank[b]);
+      const int4 r1 = *reinterpret_cast<const int4*>(&s_rank[b + 4]);
+      const int4 c0 = *reinterpret_cast<const int4*>(&s_cnt[b]);
+      const int4 c1 = *reinterpret_cast<const int4*>(&s_cnt[b + 4]);
+      const int rr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      const int cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += (rr[i] == my_r && b + i < tid) ? cc[i] : 0;
     }
-    expert_offsets[e] = acc;
+    expert_offsets[tid] = s_roff[my_r] + acc;
   }
-  for (int r = tid; r <= R; r += blockDim.x) {
-    int acc = 0;
-    for (int e2 = 0; e2 < E; ++e2) acc += (s_rank[e2] < r) ? s_cnt[e2] : 0;
-    rank_offsets[r] = acc;
-  }
-  for (int r = tid; r < R; r += blockDim.x) dedup[r] = s_ded[r];
 }
 
-__global__ __launch_bounds__(kPermThreads) void layout_permute_kernel(
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void layout_permute_kernel(
     const int32_t* __restrict__ idx, int T, int E, int k, int tpb, const int32_t* __restrict__ base,
     const int32_t* __restrict__ expert_offsets, int32_t* __restrict__ pos,
     int32_t* __restrict__ src) {
+  constexpr int kThreads = WAVES * kWave;
   extern __shared__ int smem[];
-  int* run = smem;                       // [E] next free row of each expert
-  int* wcnt = smem + E;                  // [waves][E] pairs per expert in a wave
-  int* wtag = smem + E + kPermWaves * E; // [waves][E] round that wrote wcnt
+  int* run = smem;                   // [E] next free row of each expert
+  int* wcnt = smem + E;              // [WAVES][E] pairs per expert in a wave
+  int* wtag = smem + E + WAVES * E;  // [WAVES][E] round that wrote wcnt
   const int b = blockIdx.x;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     run[e] = expert_offsets[e] + base[(size_t)b * E + e];
 #pragma unroll
-    for (int w = 0; w < kPermWaves; ++w) wtag[w * E + e] = 0;
+    for (int w = 0; w < WAVES; ++w) wtag[w * E + e] = 0;
   }
   __syncthreads();
 
@@ -170,11 +248,13 @@ __global__ __launch_bounds__(kPermThreads) void layout_permute_kernel(
   const int64_t i1 = min((int64_t)T * k, i0 + (int64_t)tpb * k);
   const int n_items = T * k;
   int tag = 0;
-  for (int64_t r0 = i0; r0 < i1; r0 += kPermThreads) {
+  int e_next = (i0 + threadIdx.x < i1) ? idx[i0 + threadIdx.x] : 0;  // next round's expert, prefetched
+  for (int64_t r0 = i0; r0 < i1; r0 += kThreads) {
     ++tag;
     const int64_t i = r0 + threadIdx.x;
     const bool valid = i < i1;
-    const int e = valid ? clamp_expert(idx[i], E) : 0;
+    const int e = valid ? clamp_expert(e_next, E) : 0;
+    if (i + kThreads < i1) e_next = idx[i + kThreads];
     uint64_t peers = ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool x = (e >> bit) & 1;
@@ -208,10 +288,10 @@ hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const i
                          const int32_t* rep, int maxrep, int32_t* rank_of, int32_t* expert_offsets,
                          int32_t* rank_offsets, int32_t* pos, int32_t* src, int32_t* dedup,
                          int32_t* ws, hipStream_t s) {
-  const Blocking bl = blocking_for(T, E);
+  const Blocking bl = blocking_for(T, E, R);
   const int nblk = T > 0 ? bl.layout_nblk : 0;
-  int32_t* hist = ws;                           // [nblk, E]
-  int32_t* ded = ws + (size_t)bl.layout_nblk * E; // [nblk, R]
+  int32_t* hist = ws;                              // [nblk, E]
+  int32_t* ded = ws + (size_t)bl.layout_nblk * E;  // [nblk, R]
   if (nblk > 0) {
     layout_count_kernel<<<nblk, kCountThreads, (2 * E + R) * sizeof(int), s>>>(
         idx, T, E, k, R, bl.layout_tpb, assign, rep, maxrep, hist, ded);
@@ -222,8 +302,14 @@ hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const i
                                                rank_of, expert_offsets, rank_offsets, dedup);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
-  layout_permute_kernel<<<nblk, kPermThreads, (1 + 2 * kPermWaves) * E * sizeof(int), s>>>(
-      idx, T, E, k, bl.layout_tpb, hist, expert_offsets, pos, src);
+  // 16 waves per permute block when blocks hold many pairs and the per-wave
+  // LDS tables (33 E ints) fit comfortably; else 4 waves (9 E ints)
+  if (E <= 256 && (int64_t)bl.layout_tpb * k >= 1024)
+    layout_permute_kernel<16><<<nblk, 16 * kWave, 33 * E * sizeof(int), s>>>(
+        idx, T, E, k, bl.layout_tpb, hist, expert_offsets, pos, src);
+  else
+    layout_permute_kernel<4><<<nblk, 4 * kWave, 9 * E * sizeof(int), s>>>(
+        idx, T, E, k, bl.layout_tpb, hist, expert_offsets, pos, src);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ namespace {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteTargetBlocks = 512;
 
-template <int L, int V>
+template <int L, int V, int ITER>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int tpb, int32_t* __restrict__ idx,
     float* __restrict__ w, int32_t* __restrict__ block_hist) {
@@ -43,55 +43,63 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   const int t_begin = blockIdx.x * tpb;
   const int t_end = min(T, t_begin + tpb);
 
-  for (int t0 = t_begin + wave * TPW; t0 < t_end; t0 += nwaves * TPW) {
-    const int t = t0 + grp;
-    const bool valid = t < t_end;
-    uint32_t key[V];
+  // Wave steps s = 0, 1, ... cover tokens t_begin + (s * nwaves + wave) * TPW.
+  // ITER steps are loaded together before any is processed.
+  for (int s0 = 0; t_begin + (s0 * nwaves + wave) * TPW < t_end; s0 += ITER) {
+    uint32_t key[ITER][V];
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int e = sl + v * L;
-      key[v] = (valid && e < E) ? logit_key(logits[(size_t)t * E + e]) : 0u;
-    }
-
-    int my_e = 0;
-    uint32_t my_key = 0u, top_key = 0u;
-    for (int j = 0; j < k; ++j) {
-      uint32_t best = key[0];
-#pragma unroll
-      for (int v = 1; v < V; ++v) best = key[v] > best ? key[v] : best;
-      best = group_max<L>(best);
-      // lowest expert id e = v*L + lane-in-group whose key equals the maximum
-      int e_sel = 0;
-      bool found = false;
+    for (int it = 0; it < ITER; ++it) {
+      const int t = t_begin + ((s0 + it) * nwaves + wave) * TPW + grp;
+      const bool valid = t < t_end;
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const uint64_t m = ballot(key[v] == best) & gmask;
-        if (!found && m != 0ull) {
-          e_sel = v * L + (__builtin_ctzll(m) - grp * L);
-          found = true;
-        }
+        const int e = sl + v * L;
+        key[it][v] = (valid && e < E) ? logit_key(logits[(size_t)t * E + e]) : 0u;
       }
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (v * L + sl == e_sel) key[v] = 0u;  // taken: never chosen again
-      if (sl == j) {
-        my_e = e_sel;
-        my_key = best;
-      }
-      if (j == 0) top_key = best;
     }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int t = t_begin + ((s0 + it) * nwaves + wave) * TPW + grp;
+      const bool valid = t < t_end;
+      int my_e = 0;
+      uint32_t my_key = 0u, top_key = 0u;
+      for (int j = 0; j < k; ++j) {
+        uint32_t best = key[it][0];
+#pragma unroll
+        for (int v = 1; v < V; ++v) best = key[it][v] > best ? key[it][v] : best;
+        best = group_max<L>(best);
+        // lowest expert id e = v*L + lane-in-group whose key equals the maximum
+        int e_sel = 0;
+        bool found = false;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const uint64_t m = ballot(key[it][v] == best) & gmask;
+          if (!found && m != 0ull) {
+            e_sel = v * L + (__builtin_ctzll(m) - grp * L);
+            found = true;
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          if (v * L + sl == e_sel) key[it][v] = 0u;  // taken: never chosen again
+        if (sl == j) {
+          my_e = e_sel;
+          my_key = best;
+        }
+        if (j == 0) top_key = best;
+      }
 
-    // softmax over the k selected logits in fp64, lanes 0..k-1 of the group
-    double ex = 0.0;
-    if (sl < k) ex = exp(static_cast<double>(key_logit(my_key)) -
-                         static_cast<double>(key_logit(top_key)));
-    double sum = 0.0;
-    for (int j = 0; j < k; ++j) sum += __shfl(ex, grp * L + j, kWave);
-    if (valid && sl < k) {
-      const size_t o = (size_t)t * k + sl;
-      idx[o] = my_e;
-      w[o] = static_cast<float>(ex / sum);
-      atomicAdd(&s_hist[my_e], 1);
+      // softmax over the k selected logits in fp64, lanes 0..k-1 of the group
+      double ex = 0.0;
+      if (sl < k) ex = exp(static_cast<double>(key_logit(my_key)) -
+                           static_cast<double>(key_logit(top_key)));
+      const double sum = group_sum16_f64<L>(ex);  // lanes >= k hold 0
+      if (valid && sl < k) {
+        const size_t o = (size_t)t * k + sl;
+        idx[o] = my_e;
+        w[o] = static_cast<float>(ex / sum);
+        atomicAdd(&s_hist[my_e], 1);
+      }
     }
   }
   __syncthreads();
@@ -100,22 +108,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 }
 
 // out[c] = sum over rows of M[rows, cols]; one block per 64 columns, the 16
-// waves split the rows and meet in LDS. Deterministic, no atomics.
+// waves split the rows (at most kSumSeg each) and meet in LDS. Each lane
+// issues its whole segment of loads at once. Deterministic, no atomics.
+constexpr int kSumSeg = 32;  // route blocks <= 16 * 32 = 512 (see blocking_for)
+
 __global__ __launch_bounds__(1024) void column_sum_kernel(const int32_t* __restrict__ M, int rows,
                                                           int cols, int32_t* __restrict__ out) {
   __shared__ int part[16][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int c = blockIdx.x * kWave + lane;
+  const int seg = (rows + 15) / 16;
+  const int r_lo = min(rows, wave * seg), r_hi = min(rows, r_lo + seg);
   int acc = 0;
   if (c < cols) {
-    int r = wave;
-    for (; r + 48 < rows; r += 64) {
-      const int a = M[(size_t)r * cols + c], b = M[(size_t)(r + 16) * cols + c];
-      const int d = M[(size_t)(r + 32) * cols + c], f = M[(size_t)(r + 48) * cols + c];
-      acc += (a + b) + (d + f);
+#pragma unroll
+    for (int i = 0; i < kSumSeg; ++i) {
+      const int r = r_lo + i;
+      acc += (r < r_hi) ? M[(size_t)r * cols + c] : 0;
     }
-    for (; r < rows; r += 16) acc += M[(size_t)r * cols + c];
   }
   part[wave][lane] = acc;
   __syncthreads();
@@ -127,11 +138,21 @@ __global__ __launch_bounds__(1024) void column_sum_kernel(const int32_t* __restr
   }
 }
 
+// Token steps loaded together: as many as a wave has (up to 4), fewer for
+// wide rows so the keys stay in registers.
 template <int L, int V>
 hipError_t launch_topk(const float* logits, int T, int E, int k, int tpb, int nblk, int32_t* idx,
                        float* w, int32_t* ws, hipStream_t s) {
-  route_topk_kernel<L, V><<<nblk, kRouteThreads, E * sizeof(int), s>>>(logits, T, E, k, tpb, idx, w,
-                                                                       ws);
+  const int steps = tpb / ((kWave / L) * (kRouteThreads / kWave));
+  const int cap = V <= 4 ? 4 : (V <= 8 ? 2 : 1);
+  const int iter = steps < cap ? steps : cap;
+  const size_t lds = E * sizeof(int);
+  if (iter >= 4)
+    route_topk_kernel<L, V, (V <= 4 ? 4 : 1)><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
+  else if (iter >= 2)
+    route_topk_kernel<L, V, (V <= 8 ? 2 : 1)><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
+  else
+    route_topk_kernel<L, V, 1><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
   return hipGetLastError();
 }
 
@@ -144,7 +165,7 @@ int lanes_per_token(int E) {
 
 }  // namespace
 
-Blocking blocking_for(int T, int E) {
+Blocking blocking_for(int T, int E, int R) {
   Blocking b{};
   const int tpw = kWave / lanes_per_token(E);
   const int step = tpw * (kRouteThreads / kWave);
@@ -153,15 +174,21 @@ Blocking blocking_for(int T, int E) {
   if (tpb < step) tpb = step;
   b.route_tpb = tpb;
   b.route_nblk = (T + tpb - 1) / tpb;
+  // The layout plan scans [blocks, E] and [blocks, R] in tasks of 64 columns
+  // with 16 waves; each wave may own at most 48 rows of one task, so the
+  // block count is capped at 48 * (waves per task), and at 256.
+  const int tasks = (E + kWave - 1) / kWave + (R + kWave - 1) / kWave;
+  const int waves_per_task = tasks >= 16 ? 1 : 16 / tasks;
+  const int max_nblk = 48 * waves_per_task < 256 ? 48 * waves_per_task : 256;
   int ltpb = 64;
-  while ((T + ltpb - 1) / ltpb > 256) ltpb *= 2;
+  while ((T + ltpb - 1) / ltpb > max_nblk) ltpb *= 2;
   b.layout_tpb = ltpb;
   b.layout_nblk = (T + ltpb - 1) / ltpb;
   return b;
 }
 
 size_t workspace_bytes(int T, int E, int R) {
-  const Blocking b = blocking_for(T, E);
+  const Blocking b = blocking_for(T, E, R);
   const size_t route = (size_t)b.route_nblk * E * sizeof(int32_t);
   const size_t layout = (size_t)b.layout_nblk * (E + R) * sizeof(int32_t);
   size_t n = route > layout ? route : layout;
@@ -171,7 +198,7 @@ size_t workspace_bytes(int T, int E, int R) {
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                         int32_t* counts, int32_t* ws, hipStream_t s) {
-  const Blocking b = blocking_for(T, E);
+  const Blocking b = blocking_for(T, E, 1);
   hipError_t err = hipSuccess;
   if (T > 0) {
     const int L = lanes_per_token(E);

@@ -29,22 +29,44 @@ constexpr int kRowThreads = 256;
 __device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
 __device__ __forceinline__ u32x4 to_vec(uint4 v) { return u32x4{v.x, v.y, v.z, v.w}; }
 
-template <int U>
-__global__ __launch_bounds__(kRowThreads) void dispatch_kernel(
+// Row teams. With ONE = true a block is one row: the row index is uniform,
+// so the row's pos / w / src entries come through scalar loads and the lane
+// stride is the compile-time block size. With ONE = false (rows shorter than
+// 64 chunks) a block holds NT / tpt rows of tpt lanes each.
+template <int NT, bool ONE>
+__device__ __forceinline__ void row_team(int tpt, int& row, int& lane, int& stride) {
+  if constexpr (ONE) {
+    row = blockIdx.x;
+    lane = threadIdx.x;
+    stride = NT;
+  } else {
+    row = blockIdx.x * (NT / tpt) + threadIdx.x / tpt;
+    lane = threadIdx.x % tpt;
+    stride = tpt;
+  }
+}
+
+// Each lane loads its U chunks of the token row, then stores them to the
+// row's k send rows.
+template <int NT, int U, bool ONE>
+__global__ __launch_bounds__(NT) void dispatch_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ send, int T,
     int k, int cpr, int tpt) {
-  const int n_rows = T * k;
-  const int per_blk = kRowThreads / tpt;
-  const int t = blockIdx.x * per_blk + threadIdx.x / tpt;
+  // Dynamic LDS is only allocated for a kernel that declares it; the launch
+  // may reserve some here to cap how many blocks share a CU. Never accessed.
+  extern __shared__ int occupancy_reserve[];
+  if (cpr < 0) occupancy_reserve[threadIdx.x] = 0;
+  int t, lt, stride;
+  row_team<NT, ONE>(tpt, t, lt, stride);
   if (t >= T) return;
-  const int lt = threadIdx.x % tpt;
+  const int n_rows = T * k;
   const u32x4* xr = x + (size_t)t * cpr;
   const int32_t* pr = pos + (size_t)t * k;
-  for (int c0 = lt; c0 < cpr; c0 += tpt * U) {
+  for (int c0 = lt; c0 < cpr; c0 += stride * U) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * tpt;
+      const int c = c0 + u * stride;
       if (c < cpr) v[u] = __builtin_nontemporal_load(xr + c);
     }
     for (int j = 0; j < k; ++j) {
@@ -53,27 +75,26 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_kernel(
       u32x4* dst = send + (size_t)r * cpr;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * tpt;
+        const int c = c0 + u * stride;
         if (c < cpr) __builtin_nontemporal_store(v[u], dst + c);
       }
     }
   }
 }
 
-template <int ACT>
+template <int ACT, bool ONE>
 __global__ __launch_bounds__(kRowThreads) void standin_kernel(
     const u32x4* send, const int32_t* __restrict__ src, const int32_t* __restrict__ idx, u32x4* y,
     int n, int E, int cpr, int tpt) {  // y may alias send: each chunk is read, then written, by one lane
-  const int per_blk = kRowThreads / tpt;
-  const int r = blockIdx.x * per_blk + threadIdx.x / tpt;
+  int r, lt, stride;
+  row_team<kRowThreads, ONE>(tpt, r, lt, stride);
   if (r >= n) return;
-  const int lt = threadIdx.x % tpt;
   const int sr = src[r];
   const int e = static_cast<unsigned>(sr) < static_cast<unsigned>(n) ? idx[sr] : 0;
   const float scale = 1.0f + static_cast<float>(e) / static_cast<float>(E);
   const u32x4* in = send + (size_t)r * cpr;
   u32x4* out = y + (size_t)r * cpr;
-  for (int c = lt; c < cpr; c += tpt) {
+  for (int c = lt; c < cpr; c += stride) {
     float f[8];
     unpack8<ACT>(to_uint4(__builtin_nontemporal_load(in + c)), f);
 #pragma unroll
@@ -82,86 +103,198 @@ __global__ __launch_bounds__(kRowThreads) void standin_kernel(
   }
 }
 
-template <int ACT, int KMAX, bool OUT_F32>
+template <int ACT, bool OUT_F32>
+__device__ __forceinline__ void combine_store(void* __restrict__ out, size_t chunk, const float (&acc)[8]) {
+  if constexpr (OUT_F32) {
+    f32x4* o = reinterpret_cast<f32x4*>(out) + chunk * 2;
+    __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, o);
+    __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, o + 1);
+  } else {
+    __builtin_nontemporal_store(to_vec(pack8<ACT>(acc)), reinterpret_cast<u32x4*>(out) + chunk);
+  }
+}
+
+// out[t] = sum_j (ascending) w[t,j] * y[pos[t,j]] in fp32. Two code shapes,
+// each the faster one where it is used (measured on MI355X, cold cache):
+//  - U == 1: per chunk position, the k row loads, then the math and store;
+//    the token's pos / w entries are read per slot (scalar loads when the
+//    row index is uniform). Used for short rows and rows of <= 256 chunks
+//    (H = 2048, k = 6: 83 us against 96 us for the batched shape).
+//  - U == 2 (one-row blocks, rows of more than 256 chunks): lanes 0..k-1 of
+//    each wave fetch the k pos / w entries in one vector load and broadcast
+//    them with readlane; each lane then issues the loads of two chunk
+//    positions before any math; with EXACT, k == KMAX is a compile-time
+//    constant so no slot is guarded (H = 4096, k = 2: 69 us against 73 us;
+//    H = 7168, k = 8: 1.58 ms against 1.62 ms).
+template <int ACT, int KMAX, bool OUT_F32, bool ONE, int U, bool EXACT>
 __global__ __launch_bounds__(kRowThreads) void combine_kernel(
     const u32x4* __restrict__ y, const int32_t* __restrict__ pos, const float* __restrict__ w,
-    void* __restrict__ out, int T, int k, int cpr, int tpt) {
-  const int per_blk = kRowThreads / tpt;
-  const int t = blockIdx.x * per_blk + threadIdx.x / tpt;
+    void* __restrict__ out, int T, int k_rt, int cpr, int tpt) {
+  const int k = EXACT ? KMAX : k_rt;
+  int t, lt, stride;
+  row_team<kRowThreads, ONE>(tpt, t, lt, stride);
   if (t >= T) return;
-  const int lt = threadIdx.x % tpt;
   size_t row[KMAX];
   float wt[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
-      const int r = pos[(size_t)t * k + j];
-      const bool ok = static_cast<unsigned>(r) < static_cast<unsigned>(T * k);
-      row[j] = ok ? (size_t)r * cpr : 0;  // a bad pos reads row 0 with weight 0
-      wt[j] = ok ? w[(size_t)t * k + j] : 0.0f;
-    }
-  }
-  for (int c = lt; c < cpr; c += tpt) {
-    u32x4 v[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (j < k) v[j] = __builtin_nontemporal_load(y + row[j] + c);
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  if constexpr (U == 1) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (j < k) {
-        float f[8];
-        unpack8<ACT>(to_uint4(v[j]), f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt[j], f[i], acc[i]);
+        const int r = pos[(size_t)t * k + j];
+        const bool ok = static_cast<unsigned>(r) < static_cast<unsigned>(T * k);
+        row[j] = ok ? (size_t)r * cpr : 0;  // a bad pos reads row 0 with weight 0
+        wt[j] = ok ? w[(size_t)t * k + j] : 0.0f;
       }
     }
-    if constexpr (OUT_F32) {
-      f32x4* o = reinterpret_cast<f32x4*>(out) + ((size_t)t * cpr + c) * 2;
-      __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, o);
-      __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, o + 1);
-    } else {
-      u32x4* o = reinterpret_cast<u32x4*>(out) + (size_t)t * cpr + c;
-      __builtin_nontemporal_store(to_vec(pack8<ACT>(acc)), o);
+    for (int c = lt; c < cpr; c += stride) {
+      u32x4 v[KMAX];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k) v[j] = __builtin_nontemporal_load(y + row[j] + c);
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+          float f[8];
+          unpack8<ACT>(to_uint4(v[j]), f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt[j], f[i], acc[i]);
+        }
+      }
+      combine_store<ACT, OUT_F32>(out, (size_t)t * cpr + c, acc);
+    }
+  } else {
+    static_assert(ONE, "the batched shape needs one row per block");
+    const int ln = __lane_id();
+    const int my_r = ln < k ? pos[(size_t)t * k + ln] : 0;
+    const float my_w = ln < k ? w[(size_t)t * k + ln] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k) {
+        const int r = __builtin_amdgcn_readlane(my_r, j);
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+        const bool ok = static_cast<unsigned>(r) < static_cast<unsigned>(T * k);
+        row[j] = ok ? (size_t)r * cpr : 0;  // a bad pos reads row 0 with weight 0
+        wt[j] = ok ? wj : 0.0f;
+      }
+    }
+    for (int c0 = lt; c0 < cpr; c0 += stride * U) {
+      u32x4 v[U][KMAX];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * stride;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (j < k && c < cpr) v[u][j] = __builtin_nontemporal_load(y + row[j] + c);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * stride;
+        if (c >= cpr) break;
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (j < k) {
+            float f[8];
+            unpack8<ACT>(to_uint4(v[u][j]), f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt[j], f[i], acc[i]);
+          }
+        }
+        combine_store<ACT, OUT_F32>(out, (size_t)t * cpr + c, acc);
+      }
     }
   }
 }
 
-// Threads per row: enough for one 16-byte chunk each, at most the block.
+// Rows of at least this many 16-byte chunks get a block each.
+constexpr int kOneRowChunks = 64;
+
+// Threads per row for short rows: enough for one 16-byte chunk each.
 int threads_per_row(int cpr) {
   int tpt = 16;
   while (tpt < cpr && tpt < kRowThreads) tpt *= 2;
   return tpt;
 }
 
-template <int ACT, bool OUT_F32>
+template <int ACT, bool OUT_F32, bool ONE>
 hipError_t launch_combine_k(const u32x4* y, const int32_t* pos, const float* w, void* out, int T,
                             int k, int cpr, int tpt, int grid, hipStream_t s) {
-  if (k <= 1) combine_kernel<ACT, 1, OUT_F32><<<grid, kRowThreads, 0, s>>>(y, pos, w, out, T, k, cpr, tpt);
-  else if (k <= 2) combine_kernel<ACT, 2, OUT_F32><<<grid, kRowThreads, 0, s>>>(y, pos, w, out, T, k, cpr, tpt);
-  else if (k <= 4) combine_kernel<ACT, 4, OUT_F32><<<grid, kRowThreads, 0, s>>>(y, pos, w, out, T, k, cpr, tpt);
-  else if (k <= 8) combine_kernel<ACT, 8, OUT_F32><<<grid, kRowThreads, 0, s>>>(y, pos, w, out, T, k, cpr, tpt);
-  else combine_kernel<ACT, 16, OUT_F32><<<grid, kRowThreads, 0, s>>>(y, pos, w, out, T, k, cpr, tpt);
+#define MOE_COMBINE(KM, ONE_, U, EX) \
+  combine_kernel<ACT, KM, OUT_F32, ONE_, U, EX><<<grid, kRowThreads, 0, s>>>(y, pos, w, out, T, k, cpr, tpt)
+  if (ONE && cpr > kRowThreads && k <= 8) {  // the batched shape, exact k
+    switch (k) {
+      case 1: MOE_COMBINE(1, true, 2, true); break;
+      case 2: MOE_COMBINE(2, true, 2, true); break;
+      case 3: MOE_COMBINE(3, true, 2, true); break;
+      case 4: MOE_COMBINE(4, true, 2, true); break;
+      case 5: MOE_COMBINE(5, true, 2, true); break;
+      case 6: MOE_COMBINE(6, true, 2, true); break;
+      case 7: MOE_COMBINE(7, true, 2, true); break;
+      default: MOE_COMBINE(8, true, 2, true); break;
+    }
+  } else if (k <= 2) {
+    MOE_COMBINE(2, ONE, 1, false);
+  } else if (k <= 4) {
+    MOE_COMBINE(4, ONE, 1, false);
+  } else if (k <= 8) {
+    MOE_COMBINE(8, ONE, 1, false);
+  } else {
+    MOE_COMBINE(16, ONE, 1, false);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 
+template <int ACT, bool OUT_F32>
+hipError_t launch_combine_a(const u32x4* y, const int32_t* pos, const float* w, void* out, int T,
+                            int k, int cpr, hipStream_t s) {
+  if (cpr >= kOneRowChunks) return launch_combine_k<ACT, OUT_F32, true>(y, pos, w, out, T, k, cpr, kRowThreads, T, s);
+  const int tpt = threads_per_row(cpr);
+  const int per_blk = kRowThreads / tpt;
+  return launch_combine_k<ACT, OUT_F32, false>(y, pos, w, out, T, k, cpr, tpt, (T + per_blk - 1) / per_blk, s);
+}
+
 }  // namespace
+
+// Launch shape of the dispatch, from measurements on MI355X (cold cache):
+//  - rows of at most 512 chunks (H <= 4096): 256-thread blocks, one row per
+//    block (several for rows under 64 chunks), and a 48 KiB LDS reservation
+//    that the kernel never touches, so at most 3 blocks share a CU. Fewer concurrent
+//    scattered row streams wrote ~10% faster than full occupancy (H = 4096,
+//    k = 2: 71 vs 80 us; H = 2048, k = 6: 86 vs 97 us).
+//  - longer rows (H = 7168): 128-thread blocks with ceil(cpr / 128) chunks
+//    per lane at full occupancy, which measured best there (1.62 vs 1.72 ms).
+constexpr size_t kDispatchLdsReserve = 48 * 1024;
 
 hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T, int k, int H,
                            hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int cpr = H / 8;
-  const int tpt = threads_per_row(cpr);
-  const int per_blk = kRowThreads / tpt;
-  const int grid = (T + per_blk - 1) / per_blk;
-  const int per_lane = (cpr + tpt - 1) / tpt;
   const u32x4* xv = static_cast<const u32x4*>(x);
   u32x4* sv = static_cast<u32x4*>(send);
-  if (per_lane <= 1) dispatch_kernel<1><<<grid, kRowThreads, 0, s>>>(xv, pos, sv, T, k, cpr, tpt);
-  else if (per_lane <= 2) dispatch_kernel<2><<<grid, kRowThreads, 0, s>>>(xv, pos, sv, T, k, cpr, tpt);
-  else dispatch_kernel<4><<<grid, kRowThreads, 0, s>>>(xv, pos, sv, T, k, cpr, tpt);
+  const size_t res = kDispatchLdsReserve;
+  if (cpr < kOneRowChunks) {
+    const int tpt = threads_per_row(cpr);
+    const int per_blk = kRowThreads / tpt;
+    dispatch_kernel<kRowThreads, 1, false><<<(T + per_blk - 1) / per_blk, kRowThreads, res, s>>>(
+        xv, pos, sv, T, k, cpr, tpt);
+  } else if (cpr <= 256) {
+    dispatch_kernel<kRowThreads, 1, true><<<T, kRowThreads, res, s>>>(xv, pos, sv, T, k, cpr, 0);
+  } else if (cpr <= 512) {
+    dispatch_kernel<kRowThreads, 2, true><<<T, kRowThreads, res, s>>>(xv, pos, sv, T, k, cpr, 0);
+  } else {
+    // ceil(cpr / 128) chunks per lane (a loop covers rows beyond 8 * 128)
+    const int u = (cpr + 127) / 128;
+    if (u <= 5) dispatch_kernel<128, 5, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
+    else if (u == 6) dispatch_kernel<128, 6, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
+    else if (u == 7) dispatch_kernel<128, 7, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
+    else dispatch_kernel<128, 8, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
+  }
   return hipGetLastError();
 }
 
@@ -170,13 +303,18 @@ hipError_t launch_standin(const void* send, const int32_t* src, const int32_t* i
   const int n = T * k;
   if (n == 0) return hipSuccess;
   const int cpr = H / 8;
-  const int tpt = threads_per_row(cpr);
-  const int per_blk = kRowThreads / tpt;
-  const int grid = (n + per_blk - 1) / per_blk;
   const u32x4* in = static_cast<const u32x4*>(send);
   u32x4* out = static_cast<u32x4*>(y);
-  if (act == 1) standin_kernel<1><<<grid, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, tpt);
-  else standin_kernel<2><<<grid, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, tpt);
+  if (cpr >= kOneRowChunks) {
+    if (act == 1) standin_kernel<1, true><<<n, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, 0);
+    else standin_kernel<2, true><<<n, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, 0);
+  } else {
+    const int tpt = threads_per_row(cpr);
+    const int per_blk = kRowThreads / tpt;
+    const int grid = (n + per_blk - 1) / per_blk;
+    if (act == 1) standin_kernel<1, false><<<grid, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, tpt);
+    else standin_kernel<2, false><<<grid, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, tpt);
+  }
   return hipGetLastError();
 }
 
@@ -184,15 +322,12 @@ hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, voi
                           int H, int act, bool out_f32, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int cpr = H / 8;
-  const int tpt = threads_per_row(cpr);
-  const int per_blk = kRowThreads / tpt;
-  const int grid = (T + per_blk - 1) / per_blk;
   const u32x4* yv = static_cast<const u32x4*>(y);
   if (act == 1)
-    return out_f32 ? launch_combine_k<1, true>(yv, pos, w, out, T, k, cpr, tpt, grid, s)
-                   : launch_combine_k<1, false>(yv, pos, w, out, T, k, cpr, tpt, grid, s);
-  return out_f32 ? launch_combine_k<2, true>(yv, pos, w, out, T, k, cpr, tpt, grid, s)
-                 : launch_combine_k<2, false>(yv, pos, w, out, T, k, cpr, tpt, grid, s);
+    return out_f32 ? launch_combine_a<1, true>(yv, pos, w, out, T, k, cpr, s)
+                   : launch_combine_a<1, false>(yv, pos, w, out, T, k, cpr, s);
+  return out_f32 ? launch_combine_a<2, true>(yv, pos, w, out, T, k, cpr, s)
+                 : launch_combine_a<2, false>(yv, pos, w, out, T, k, cpr, s);
 }
 
 }  // namespace moe
