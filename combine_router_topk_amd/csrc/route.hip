@@ -6,11 +6,12 @@
 //
 // Kernel 1 (route_topk): a group of L lanes owns one token's row of E logits
 // (V = E/L values per lane, coalesced loads). Each of the k rounds takes the
-// group maximum of order-preserving 32-bit keys with xor shuffles and then
-// the lowest expert id holding that key with ballots, so ties resolve to the
-// lower id without 64-bit shuffles. Lane j of the group keeps slot j; the
-// softmax over the selected logits is evaluated in fp64 by lanes 0..k-1 in
-// parallel and summed in ascending slot order. Selections are counted in an
+// group maximum of order-preserving 32-bit keys with DPP butterflies (and
+// readlane across 16-lane rows) and then the lowest expert id holding that
+// key with ballots, so ties resolve to the lower id without 64-bit
+// exchanges. Lane j of the group keeps slot j; the softmax over the selected
+// logits is evaluated in fp64 by lanes 0..k-1 in parallel and summed with a
+// fixed-order DPP tree. Selections are counted in an
 // LDS histogram per block, written as one row of a [blocks, E] matrix: no
 // global atomics.
 // Kernel 2 (column_sum): counts[e] = sum of column e of that matrix.
@@ -24,7 +25,7 @@ namespace {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteTargetBlocks = 512;
 
-template <int L, int V, int ITER>
+template <int L, int V>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int tpb, int32_t* __restrict__ idx,
     float* __restrict__ w, int32_t* __restrict__ block_hist) {
@@ -43,63 +44,53 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   const int t_begin = blockIdx.x * tpb;
   const int t_end = min(T, t_begin + tpb);
 
-  // Wave steps s = 0, 1, ... cover tokens t_begin + (s * nwaves + wave) * TPW.
-  // ITER steps are loaded together before any is processed.
-  for (int s0 = 0; t_begin + (s0 * nwaves + wave) * TPW < t_end; s0 += ITER) {
-    uint32_t key[ITER][V];
+  for (int t0 = t_begin + wave * TPW; t0 < t_end; t0 += nwaves * TPW) {
+    const int t = t0 + grp;
+    const bool valid = t < t_end;
+    uint32_t key[V];
 #pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int t = t_begin + ((s0 + it) * nwaves + wave) * TPW + grp;
-      const bool valid = t < t_end;
+    for (int v = 0; v < V; ++v) {
+      const int e = sl + v * L;
+      key[v] = (valid && e < E) ? logit_key(logits[(size_t)t * E + e]) : 0u;
+    }
+    int my_e = 0;
+    uint32_t my_key = 0u, top_key = 0u;
+    for (int j = 0; j < k; ++j) {
+      uint32_t best = key[0];
+#pragma unroll
+      for (int v = 1; v < V; ++v) best = key[v] > best ? key[v] : best;
+      best = group_max<L>(best);
+      // lowest expert id e = v*L + lane-in-group whose key equals the maximum
+      int e_sel = 0;
+      bool found = false;
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const int e = sl + v * L;
-        key[it][v] = (valid && e < E) ? logit_key(logits[(size_t)t * E + e]) : 0u;
+        const uint64_t m = ballot(key[v] == best) & gmask;
+        if (!found && m != 0ull) {
+          e_sel = v * L + (__builtin_ctzll(m) - grp * L);
+          found = true;
+        }
       }
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (v * L + sl == e_sel) key[v] = 0u;  // taken: never chosen again
+      if (sl == j) {
+        my_e = e_sel;
+        my_key = best;
+      }
+      if (j == 0) top_key = best;
     }
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int t = t_begin + ((s0 + it) * nwaves + wave) * TPW + grp;
-      const bool valid = t < t_end;
-      int my_e = 0;
-      uint32_t my_key = 0u, top_key = 0u;
-      for (int j = 0; j < k; ++j) {
-        uint32_t best = key[it][0];
-#pragma unroll
-        for (int v = 1; v < V; ++v) best = key[it][v] > best ? key[it][v] : best;
-        best = group_max<L>(best);
-        // lowest expert id e = v*L + lane-in-group whose key equals the maximum
-        int e_sel = 0;
-        bool found = false;
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          const uint64_t m = ballot(key[it][v] == best) & gmask;
-          if (!found && m != 0ull) {
-            e_sel = v * L + (__builtin_ctzll(m) - grp * L);
-            found = true;
-          }
-        }
-#pragma unroll
-        for (int v = 0; v < V; ++v)
-          if (v * L + sl == e_sel) key[it][v] = 0u;  // taken: never chosen again
-        if (sl == j) {
-          my_e = e_sel;
-          my_key = best;
-        }
-        if (j == 0) top_key = best;
-      }
 
-      // softmax over the k selected logits in fp64, lanes 0..k-1 of the group
-      double ex = 0.0;
-      if (sl < k) ex = exp(static_cast<double>(key_logit(my_key)) -
-                           static_cast<double>(key_logit(top_key)));
-      const double sum = group_sum16_f64<L>(ex);  // lanes >= k hold 0
-      if (valid && sl < k) {
-        const size_t o = (size_t)t * k + sl;
-        idx[o] = my_e;
-        w[o] = static_cast<float>(ex / sum);
-        atomicAdd(&s_hist[my_e], 1);
-      }
+    // softmax over the k selected logits in fp64, lanes 0..k-1 of the group
+    double ex = 0.0;
+    if (sl < k) ex = exp(static_cast<double>(key_logit(my_key)) -
+                         static_cast<double>(key_logit(top_key)));
+    const double sum = group_sum16_f64<L>(ex);  // lanes >= k hold 0
+    if (valid && sl < k) {
+      const size_t o = (size_t)t * k + sl;
+      idx[o] = my_e;
+      w[o] = static_cast<float>(ex / sum);
+      atomicAdd(&s_hist[my_e], 1);
     }
   }
   __syncthreads();
@@ -138,29 +129,21 @@ __global__ __launch_bounds__(1024) void column_sum_kernel(const int32_t* __restr
   }
 }
 
-// Token steps loaded together: as many as a wave has (up to 4), fewer for
-// wide rows so the keys stay in registers.
 template <int L, int V>
 hipError_t launch_topk(const float* logits, int T, int E, int k, int tpb, int nblk, int32_t* idx,
                        float* w, int32_t* ws, hipStream_t s) {
-  const int steps = tpb / ((kWave / L) * (kRouteThreads / kWave));
-  const int cap = V <= 4 ? 4 : (V <= 8 ? 2 : 1);
-  const int iter = steps < cap ? steps : cap;
-  const size_t lds = E * sizeof(int);
-  if (iter >= 4)
-    route_topk_kernel<L, V, (V <= 4 ? 4 : 1)><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
-  else if (iter >= 2)
-    route_topk_kernel<L, V, (V <= 8 ? 2 : 1)><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
-  else
-    route_topk_kernel<L, V, 1><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
+  route_topk_kernel<L, V><<<nblk, kRouteThreads, E * sizeof(int), s>>>(logits, T, E, k, tpb, idx, w, ws);
   return hipGetLastError();
 }
 
+// Lanes per token: about four logits per lane measured fastest (T = 65536,
+// E = 256, k = 8: 56 us at 64 lanes x 4 against 74 us at 16 x 16 and 85 us at
+// 32 x 8; T = 16384, E = 64, k = 2: 6.6 us at 16 x 4 against 8.2 us at 64 x 1).
+// At least 16 lanes, so lanes 0..k-1 can hold the k <= 16 slots.
 int lanes_per_token(int E) {
-  if (E <= 8) return 8;
-  if (E <= 16) return 16;
-  if (E <= 32) return 32;
-  return 64;
+  int L = 16;
+  while (L < 64 && L * 4 < E) L *= 2;
+  return L;
 }
 
 }  // namespace
@@ -202,14 +185,14 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
   hipError_t err = hipSuccess;
   if (T > 0) {
     const int L = lanes_per_token(E);
+    const int V = (E + L - 1) / L;  // L = 16: 1..4; 32: 3..4; 64: 3..16
     const int tpb = b.route_tpb, n = b.route_nblk;
-    if (L == 8) err = launch_topk<8, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else if (L == 16) err = launch_topk<16, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else if (L == 32) err = launch_topk<32, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else if (E <= 64) err = launch_topk<64, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else if (E <= 128) err = launch_topk<64, 2>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else if (E <= 256) err = launch_topk<64, 4>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else if (E <= 512) err = launch_topk<64, 8>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    if (L == 16 && V == 1) err = launch_topk<16, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else if (L == 16 && V == 2) err = launch_topk<16, 2>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else if (L == 16) err = launch_topk<16, 4>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else if (L == 32) err = launch_topk<32, 4>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else if (V <= 4) err = launch_topk<64, 4>(logits, T, E, k, tpb, n, idx, w, ws, s);
+    else if (V <= 8) err = launch_topk<64, 8>(logits, T, E, k, tpb, n, idx, w, ws, s);
     else err = launch_topk<64, 16>(logits, T, E, k, tpb, n, idx, w, ws, s);
     if (err != hipSuccess) return err;
   }

@@ -47,8 +47,11 @@ __device__ __forceinline__ void row_team(int tpt, int& row, int& lane, int& stri
 }
 
 // Each lane loads its U chunks of the token row, then stores them to the
-// row's k send rows.
-template <int NT, int U, bool ONE>
+// row's k send rows. With SERIAL, each load completes before the next is
+// issued: for long rows with many copies (H = 7168, k = 8: 56 stores per
+// lane) this staggers the waves' store bursts and measured 7% faster
+// (1.63 vs 1.76 ms); for shorter rows it does not help.
+template <int NT, int U, bool ONE, bool SERIAL = false>
 __global__ __launch_bounds__(NT) void dispatch_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ send, int T,
     int k, int cpr, int tpt) {
@@ -68,6 +71,7 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * stride;
       if (c < cpr) v[u] = __builtin_nontemporal_load(xr + c);
+      if constexpr (SERIAL) __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     for (int j = 0; j < k; ++j) {
       const int r = pr[j];
@@ -268,7 +272,8 @@ hipError_t launch_combine_a(const u32x4* y, const int32_t* pos, const float* w, 
 //    scattered row streams wrote ~10% faster than full occupancy (H = 4096,
 //    k = 2: 71 vs 80 us; H = 2048, k = 6: 86 vs 97 us).
 //  - longer rows (H = 7168): 128-thread blocks with ceil(cpr / 128) chunks
-//    per lane at full occupancy, which measured best there (1.62 vs 1.72 ms).
+//    per lane at full occupancy and serialized row loads, which measured
+//    best there (1.63 ms against 1.69-1.77 ms for the other shapes).
 constexpr size_t kDispatchLdsReserve = 48 * 1024;
 
 hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T, int k, int H,
@@ -290,10 +295,10 @@ hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T,
   } else {
     // ceil(cpr / 128) chunks per lane (a loop covers rows beyond 8 * 128)
     const int u = (cpr + 127) / 128;
-    if (u <= 5) dispatch_kernel<128, 5, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
-    else if (u == 6) dispatch_kernel<128, 6, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
-    else if (u == 7) dispatch_kernel<128, 7, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
-    else dispatch_kernel<128, 8, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
+    if (u <= 5) dispatch_kernel<128, 5, true, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
+    else if (u == 6) dispatch_kernel<128, 6, true, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
+    else if (u == 7) dispatch_kernel<128, 7, true, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
+    else dispatch_kernel<128, 8, true, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
   }
   return hipGetLastError();
 }

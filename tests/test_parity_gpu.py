@@ -75,13 +75,15 @@ def test_deterministic_bitwise():
 # ---- shapes at the edges of the kernels' blocking --------------------------
 
 EDGE = [
-    ("E1_k1_R1_H8", 1, 1, 1, 1, 8),
-    ("E5_k3_R5", 97, 5, 3, 5, 24),          # 8 lanes per token, padding lanes
+    # route lanes per token x logits per lane in the comments
+    ("E1_k1_R1_H8", 1, 1, 1, 1, 8),         # 16 x 1, one 16-byte chunk per row
+    ("E5_k3_R5", 97, 5, 3, 5, 24),          # 16 x 1, padding lanes
     ("E8_k8_fullsort", 300, 8, 8, 2, 16),   # k = E
-    ("E12_k5_R3", 513, 12, 5, 3, 40),       # 16 lanes, scale 1 + e/12 not exact
-    ("E20_k4_R4", 257, 20, 4, 4, 8),        # 32 lanes
-    ("E100_k7_R10", 611, 100, 7, 10, 72),   # 2 values per lane, padded
-    ("E1024_k16_R1024", 300, 1024, 16, 1024, 16),  # largest E, k and R
+    ("E12_k5_R3", 513, 12, 5, 3, 40),       # scale 1 + e/12 not exact in binary
+    ("E20_k4_R4", 257, 20, 4, 4, 8),        # 16 x 2
+    ("E100_k7_R10", 611, 100, 7, 10, 72),   # 32 x 4, padded
+    ("E384_k10_R12", 700, 384, 10, 12, 64), # 64 x 8, padded
+    ("E1024_k16_R1024", 300, 1024, 16, 1024, 16),  # 64 x 16; largest E, k and R
     ("T1", 1, 64, 2, 32, 4096),
 ]
 
