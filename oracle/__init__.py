@@ -24,3 +24,5 @@ from .rows import (combine, decode16, dispatch, dispatch_rows, encode16,  # noqa
 from .bytes_model import (allgather_bytes_per_gpu, alltoall_bytes_per_gpu,  # noqa: F401
                           crossover_bytes, link_time_s)
 from .pipeline import route_and_layout, rows_for  # noqa: F401
+from .single_send import (single_send_dispatch, single_send_expand,  # noqa: F401
+                          single_send_layout)
