@@ -23,7 +23,8 @@ MOE_FLAG_GREEDY_ID_ORDER = 1 << 0
 MOE_FLAG_OUT_F32 = 1 << 1
 
 EXPORTED = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
-            "moe_route", "moe_assign_replicas", "moe_layout", "moe_dispatch",
+            "moe_route", "moe_assign_replicas", "moe_layout", "moe_layout_single_send",
+            "moe_single_send_dispatch", "moe_single_send_expand", "moe_dispatch",
             "moe_expert_standin", "moe_combine")
 
 _TORCH_ACT = {MOE_F16: torch.float16, MOE_BF16: torch.bfloat16}
@@ -47,7 +48,7 @@ class Problem(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m combine_router_topk_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python combine_router_topk_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(Problem)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
@@ -59,6 +60,10 @@ def _load() -> ctypes.CDLL:
         "moe_route": (i32, [P, vp, vp, vp, vp, vp, sz, vp]),
         "moe_assign_replicas": (i32, [P, vp, vp, i32, vp, vp, vp]),
         "moe_layout": (i32, [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_layout_single_send": (i32, [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, sz, vp]),
+        "moe_single_send_dispatch": (i32, [P, vp, vp, vp, i32, vp]),
+        "moe_single_send_expand": (i32, [P, vp, vp, vp, i32, vp, vp]),
         "moe_dispatch": (i32, [P, vp, vp, vp, vp]),
         "moe_expert_standin": (i32, [P, vp, vp, vp, vp, vp]),
         "moe_combine": (i32, [P, vp, vp, vp, vp, vp]),
@@ -156,6 +161,45 @@ def moe_layout(p: Problem, idx, assign, rep, maxrep: int, rank_of, expert_offset
                            _ptr(pos, torch.int32, n, "pos"), _ptr(src, torch.int32, n, "src"),
                            _ptr(dedup, torch.int32, p.R, "dedup"), _ptr(ws, None, None, "ws"),
                            ws.numel() * ws.element_size(), _stream(stream)), "moe_layout")
+
+
+def moe_layout_single_send(p: Problem, idx, assign, rep, maxrep: int, rank_of, expert_offsets,
+                           rank_offsets, pos, src, dedup, ss_rank_offsets, ss_row, ss_token, ws,
+                           stream=None) -> None:
+    n = p.T * p.k
+    _check(_lib.moe_layout_single_send(
+        ctypes.byref(p), _ptr(idx, torch.int32, n, "idx"), _ptr(assign, torch.int32, p.E, "assign"),
+        _ptr(rep, torch.int32, p.E * maxrep if rep is not None else 0, "rep"), maxrep,
+        _ptr(rank_of, torch.int32, p.E, "rank_of"),
+        _ptr(expert_offsets, torch.int32, p.E, "expert_offsets"),
+        _ptr(rank_offsets, torch.int32, p.R + 1, "rank_offsets"),
+        _ptr(pos, torch.int32, n, "pos"), _ptr(src, torch.int32, n, "src"),
+        _ptr(dedup, torch.int32, p.R, "dedup"),
+        _ptr(ss_rank_offsets, torch.int32, p.R + 1, "ss_rank_offsets"),
+        _ptr(ss_row, torch.int32, n, "ss_row"), _ptr(ss_token, torch.int32, n, "ss_token"),
+        _ptr(ws, None, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+        "moe_layout_single_send")
+
+
+def moe_single_send_dispatch(p: Problem, x, ss_row, send_ss, stream=None) -> None:
+    """send_ss holds the single-send rows; its row count is the capacity."""
+    act = _TORCH_ACT.get(p.act_dtype)
+    cap = send_ss.shape[0] if send_ss is not None else 0
+    _check(_lib.moe_single_send_dispatch(ctypes.byref(p), _ptr(x, act, p.T * p.H, "x"),
+                                         _ptr(ss_row, torch.int32, p.T * p.k, "ss_row"),
+                                         _ptr(send_ss, act, cap * p.H, "send_ss"), cap,
+                                         _stream(stream)), "moe_single_send_dispatch")
+
+
+def moe_single_send_expand(p: Problem, send_ss, ss_row, src, send, stream=None) -> None:
+    act = _TORCH_ACT.get(p.act_dtype)
+    n = p.T * p.k
+    cap = send_ss.shape[0]
+    _check(_lib.moe_single_send_expand(ctypes.byref(p), _ptr(send_ss, act, cap * p.H, "send_ss"),
+                                       _ptr(ss_row, torch.int32, n, "ss_row"),
+                                       _ptr(src, torch.int32, n, "src"), cap,
+                                       _ptr(send, act, n * p.H, "send"), _stream(stream)),
+           "moe_single_send_expand")
 
 
 def moe_dispatch(p: Problem, x, pos, send, stream=None) -> None:

@@ -1,7 +1,9 @@
 """Builds libmoe_route.so (all HIP sources under csrc/) for gfx950 with hipcc.
 
-Run `python -m combine_router_topk_amd.build` or call build(). Objects go to
-_build/ at the repository root; the library lands next to this file.
+Run `python combine_router_topk_amd/build.py` (by path: importing the package
+loads the library) or call build() from a module loaded by path. Objects go to
+_build/ at the repository root; the library lands next to this file. The module
+imports nothing from the package.
 """
 from __future__ import annotations
 

@@ -153,7 +153,73 @@ moe_status moe_layout(const moe_problem* p, const int32_t* idx, const int32_t* a
   clear_stale_error();
   return hip_status(moe::launch_layout(idx, p->T, p->E, p->k, p->R, assign, rep, rep ? maxrep : 1,
                                        rank_of, expert_offsets, rank_offsets, pos, src, dedup,
+                                       nullptr, nullptr, nullptr, static_cast<int32_t*>(ws),
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+moe_status moe_layout_single_send(const moe_problem* p, const int32_t* idx, const int32_t* assign,
+                                  const int32_t* rep, int32_t maxrep, int32_t* rank_of,
+                                  int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos,
+                                  int32_t* src, int32_t* dedup, int32_t* ss_rank_offsets,
+                                  int32_t* ss_row, int32_t* ss_token, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  const char* fn = "moe_layout_single_send";
+  CHECK(check_problem(p, fn));
+  CHECK(check_rep(p, rep, maxrep, fn));
+  if (assign != nullptr) CHECK(need(assign, 4, fn, "assign"));
+  CHECK(need(rank_of, 4, fn, "rank_of"));
+  CHECK(need(expert_offsets, 4, fn, "expert_offsets"));
+  CHECK(need(rank_offsets, 4, fn, "rank_offsets"));
+  CHECK(need(dedup, 4, fn, "dedup"));
+  CHECK(need(ss_rank_offsets, 4, fn, "ss_rank_offsets"));
+  CHECK(need(ws, 256, fn, "ws"));
+  if (p->T > 0) {
+    CHECK(need(idx, 4, fn, "idx"));
+    CHECK(need(pos, 4, fn, "pos"));
+    CHECK(need(src, 4, fn, "src"));
+    CHECK(need(ss_row, 4, fn, "ss_row"));
+    CHECK(need(ss_token, 4, fn, "ss_token"));
+  }
+  const size_t req = moe::workspace_bytes(p->T, p->E, p->R);
+  if (ws_bytes < req) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, req);
+  clear_stale_error();
+  return hip_status(moe::launch_layout(idx, p->T, p->E, p->k, p->R, assign, rep, rep ? maxrep : 1,
+                                       rank_of, expert_offsets, rank_offsets, pos, src, dedup,
+                                       ss_rank_offsets, ss_row, ss_token,
                                        static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+moe_status moe_single_send_dispatch(const moe_problem* p, const void* x, const int32_t* ss_row,
+                                    void* send_ss, int32_t ss_capacity, void* stream) {
+  const char* fn = "moe_single_send_dispatch";
+  CHECK(check_problem(p, fn));
+  if (ss_capacity < 0) return fail(MOE_ERR_INVALID_ARG, "%s: ss_capacity=%d < 0", fn, ss_capacity);
+  if (p->T == 0 || ss_capacity == 0) return MOE_OK;
+  CHECK(need(x, 16, fn, "x"));
+  CHECK(need(ss_row, 4, fn, "ss_row"));
+  CHECK(need(send_ss, 16, fn, "send_ss"));
+  clear_stale_error();
+  return hip_status(moe::launch_single_send_dispatch(x, ss_row, send_ss, ss_capacity, p->T, p->k,
+                                                     p->H, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+moe_status moe_single_send_expand(const moe_problem* p, const void* send_ss, const int32_t* ss_row,
+                                  const int32_t* src, int32_t ss_capacity, void* send,
+                                  void* stream) {
+  const char* fn = "moe_single_send_expand";
+  CHECK(check_problem(p, fn));
+  if (ss_capacity < 0) return fail(MOE_ERR_INVALID_ARG, "%s: ss_capacity=%d < 0", fn, ss_capacity);
+  if (p->T == 0) return MOE_OK;
+  CHECK(need(send_ss, 16, fn, "send_ss"));
+  CHECK(need(ss_row, 4, fn, "ss_row"));
+  CHECK(need(src, 4, fn, "src"));
+  CHECK(need(send, 16, fn, "send"));
+  clear_stale_error();
+  return hip_status(moe::launch_single_send_expand(send_ss, ss_row, src, ss_capacity, send, p->T,
+                                                   p->k, p->H, static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -27,10 +27,20 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
 hipError_t launch_assign(const int32_t* counts, int E, int R, const int32_t* rep, int maxrep,
                          bool id_order, int32_t* assign, int32_t* active, hipStream_t s);
 
+// ss_rank_offsets, ss_row and ss_token are all null (plain layout) or all set
+// (also the single-send rows).
 hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const int32_t* assign,
                          const int32_t* rep, int maxrep, int32_t* rank_of, int32_t* expert_offsets,
                          int32_t* rank_offsets, int32_t* pos, int32_t* src, int32_t* dedup,
+                         int32_t* ss_rank_offsets, int32_t* ss_row, int32_t* ss_token,
                          int32_t* ws, hipStream_t s);
+
+hipError_t launch_single_send_dispatch(const void* x, const int32_t* ss_row, void* send_ss,
+                                       int ss_capacity, int T, int k, int H, hipStream_t s);
+
+hipError_t launch_single_send_expand(const void* send_ss, const int32_t* ss_row,
+                                     const int32_t* src, int ss_capacity, void* send, int T, int k,
+                                     int H, hipStream_t s);
 
 hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T, int k, int H,
                            hipStream_t s);

@@ -44,7 +44,7 @@ __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (
 __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     const int32_t* __restrict__ idx, int T, int E, int k, int R, int tpb,
     const int32_t* __restrict__ assign, const int32_t* __restrict__ rep, int maxrep,
-    int32_t* __restrict__ hist, int32_t* __restrict__ ded) {
+    int32_t* __restrict__ hist, int32_t* __restrict__ ded, int32_t* __restrict__ lead_mask) {
   extern __shared__ int smem[];
   int* s_rank = smem;        // [E]
   int* s_hist = smem + E;    // [E]
@@ -68,27 +68,33 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     int rk[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) rk[j] = j < k ? s_rank[clamp_expert(row[j], E)] : -1 - j;
+    int lead = 0;  // bit j: slot j is the token's first slot on its rank
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       bool seen = false;
 #pragma unroll
       for (int jj = 0; jj < j; ++jj) seen |= (rk[jj] == rk[j]);
-      if (j < k && !seen) atomicAdd(&s_ded[rk[j]], 1);
+      if (j < k && !seen) {
+        atomicAdd(&s_ded[rk[j]], 1);
+        lead |= 1 << j;
+      }
     }
+    if (lead_mask != nullptr) lead_mask[t] = lead;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = s_hist[e];
   for (int r = threadIdx.x; r < R; r += blockDim.x) ded[(size_t)blockIdx.x * R + r] = s_ded[r];
 }
 
-// Column pass over the two per-block matrices: hist [rows, E] is replaced by
-// its exclusive prefix over rows (column by column) and its column totals go
-// to s_cnt; ded [rows, R] is only summed into s_ded. The work is cut into
+// Column pass over the two per-block matrices: hist [rows, E] and ded
+// [rows, R] are replaced by their exclusive prefixes over rows (column by
+// column: the block's first row per expert, and per rank for single-send
+// rows) and their column totals go to s_cnt and s_ded. The work is cut into
 // tasks of 64 columns; the 16 waves are shared among as many tasks as fit,
 // each task's waves splitting the rows into segments of at most kSegRegs
 // rows (the layout blocking guarantees it), loaded in one batch and kept in
 // registers: one memory round trip per group of tasks.
-__device__ void column_pass(int32_t* __restrict__ hist, int E, const int32_t* __restrict__ ded, int R,
+__device__ void column_pass(int32_t* __restrict__ hist, int E, int32_t* __restrict__ ded, int R,
                             int rows, int* s_cnt, int* s_ded, int (*part)[kWave]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -106,7 +112,7 @@ __device__ void column_pass(int32_t* __restrict__ hist, int E, const int32_t* __
     const int cols = is_h ? E : R;
     const int c = (is_h ? task : task - ch_h) * kWave + lane;
     const bool col_ok = on && c < cols;
-    const int32_t* M = is_h ? hist : ded;
+    int32_t* M = is_h ? hist : ded;
     int v[kSegRegs];
     int s = 0;
 #pragma unroll
@@ -128,14 +134,12 @@ __device__ void column_pass(int32_t* __restrict__ hist, int E, const int32_t* __
     }
     if (col_ok) {
       if (sw == 0) (is_h ? s_cnt : s_ded)[c] = all;
-      if (is_h) {
-        int run = pre;
+      int run = pre;
 #pragma unroll
-        for (int i = 0; i < kSegRegs; ++i) {
-          const int r = r_lo + i;
-          if (r < r_hi) hist[(size_t)r * cols + c] = run;
-          run += v[i];
-        }
+      for (int i = 0; i < kSegRegs; ++i) {
+        const int r = r_lo + i;
+        if (r < r_hi) M[(size_t)r * cols + c] = run;
+        run += v[i];
       }
     }
     __syncthreads();
@@ -162,10 +166,11 @@ __device__ int block_excl_scan(int v, int* s_wave, int* total) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void layout_plan_kernel(
-    int T, int E, int k, int R, int nblk, int32_t* __restrict__ hist, const int32_t* __restrict__ ded,
+    int T, int E, int k, int R, int nblk, int32_t* __restrict__ hist, int32_t* __restrict__ ded,
     const int32_t* __restrict__ assign, const int32_t* __restrict__ rep, int maxrep,
     int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
-    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ dedup) {
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ dedup,
+    int32_t* __restrict__ ss_rank_offsets) {
   __shared__ __align__(16) int s_rank[kMaxE + 8];
   __shared__ __align__(16) int s_cnt[kMaxE + 8];
   __shared__ int s_ded[kMaxR];
@@ -173,6 +178,7 @@ __global__ __launch_bounds__(kPlanThreads) void layout_plan_kernel(
   __shared__ int s_roff[kMaxR];
   __shared__ int part[kPlanWaves][kWave];
   __shared__ int s_wave[kPlanWaves];
+  __shared__ int s_wave2[kPlanWaves];
   const int tid = threadIdx.x;  // E, R <= 1024 == blockDim.x: one expert / rank per thread
   // issue the expert-rank loads now, use them after the column pass
   int a_e = -1, p_e = 0;
@@ -219,6 +225,13 @@ __global__ __launch_bounds__(kPlanThreads) void layout_plan_kernel(
       for (int i = 0; i < 8; ++i) acc += (rr[i] == my_r && b + i < tid) ? cc[i] : 0;
     }
     expert_offsets[tid] = s_roff[my_r] + acc;
+  }
+  if (ss_rank_offsets != nullptr) {
+    // single-send rows: one per (token, rank), grouped by rank
+    int ss_total = 0;
+    const int ss_off = block_excl_scan(tid < R ? s_ded[tid] : 0, s_wave2, &ss_total);
+    if (tid < R) ss_rank_offsets[tid] = ss_off;
+    if (tid == 0) ss_rank_offsets[R] = ss_total;
   }
 }
 
@@ -282,24 +295,100 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_permute_kernel(
   }
 }
 
+// Single-send rows: one per (token, destination rank), grouped by rank and
+// inside a rank by token. A token's leader slot for a rank (its first slot
+// on that rank) takes the next row of the rank; its other slots on the same
+// rank reuse that row. The stable order comes from the same ballot matching
+// as the expert permutation, keyed by rank and counting leaders only: a
+// leader's row is the number of leaders of its rank before it; a non-leader
+// sees its own leader among those before it, so its row is that count - 1.
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void layout_single_send_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int R, int tpb,
+    const int32_t* __restrict__ rank_of, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ ss_rank_offsets, const int32_t* __restrict__ lead_mask,
+    int32_t* __restrict__ ss_row, int32_t* __restrict__ ss_token) {
+  constexpr int kThreads = WAVES * kWave;
+  extern __shared__ int smem[];
+  int* s_rank = smem;                       // [E]
+  int* run = smem + E;                      // [R] next free single-send row of each rank
+  int* wcnt = smem + E + R;                 // [WAVES][R] leaders per rank in a wave
+  int* wtag = smem + E + R + WAVES * R;     // [WAVES][R] round that wrote wcnt
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_rank[e] = rank_of[e];
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    run[r] = ss_rank_offsets[r] + base[(size_t)b * R + r];
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) wtag[w * R + r] = 0;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nbits = R > 1 ? 32 - __builtin_clz((unsigned)(R - 1)) : 0;
+  const uint64_t lt = lanemask_lt(lane);
+  const int64_t i0 = (int64_t)b * tpb * k;
+  const int64_t i1 = min((int64_t)T * k, i0 + (int64_t)tpb * k);
+  const int n_items = T * k;
+  int tag = 0;
+  for (int64_t r0 = i0; r0 < i1; r0 += kThreads) {
+    ++tag;
+    const int64_t i = r0 + threadIdx.x;
+    const bool valid = i < i1;
+    const int ii = static_cast<int>(i);  // pair index, below 2^31
+    const int t = valid ? ii / k : 0;
+    const int j = valid ? ii - t * k : 0;
+    const int r = valid ? s_rank[clamp_expert(idx[i], E)] : 0;
+    const bool leader = valid && ((lead_mask[t] >> j) & 1);
+    uint64_t peers = ballot(leader);  // leaders of the same rank
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool x = (r >> bit) & 1;
+      const uint64_t m = ballot(x);
+      peers &= x ? m : ~m;
+    }
+    const int before = __popcll(peers & lt);
+    const int cnt = __popcll(peers);
+    const bool writer = leader && (__builtin_ctzll(peers) == lane);
+    if (writer) {
+      wcnt[wave * R + r] = cnt;
+      wtag[wave * R + r] = tag;
+    }
+    __syncthreads();
+    if (valid) {
+      int pre = 0;
+      for (int w = 0; w < wave; ++w) pre += (wtag[w * R + r] == tag) ? wcnt[w * R + r] : 0;
+      const int q = run[r] + pre + before - (leader ? 0 : 1);
+      ss_row[i] = q;
+      if (leader && static_cast<unsigned>(q) < static_cast<unsigned>(n_items)) ss_token[q] = t;
+    }
+    __syncthreads();
+    if (writer) atomicAdd(&run[r], cnt);
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const int32_t* assign,
                          const int32_t* rep, int maxrep, int32_t* rank_of, int32_t* expert_offsets,
                          int32_t* rank_offsets, int32_t* pos, int32_t* src, int32_t* dedup,
+                         int32_t* ss_rank_offsets, int32_t* ss_row, int32_t* ss_token,
                          int32_t* ws, hipStream_t s) {
   const Blocking bl = blocking_for(T, E, R);
   const int nblk = T > 0 ? bl.layout_nblk : 0;
-  int32_t* hist = ws;                              // [nblk, E]
-  int32_t* ded = ws + (size_t)bl.layout_nblk * E;  // [nblk, R]
+  const bool ss = ss_rank_offsets != nullptr;
+  int32_t* hist = ws;                                   // [nblk, E]
+  int32_t* ded = ws + (size_t)bl.layout_nblk * E;       // [nblk, R]
+  int32_t* lead = ded + (size_t)bl.layout_nblk * R;     // [T] leader masks (single-send)
   if (nblk > 0) {
     layout_count_kernel<<<nblk, kCountThreads, (2 * E + R) * sizeof(int), s>>>(
-        idx, T, E, k, R, bl.layout_tpb, assign, rep, maxrep, hist, ded);
+        idx, T, E, k, R, bl.layout_tpb, assign, rep, maxrep, hist, ded, ss ? lead : nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   layout_plan_kernel<<<1, kPlanThreads, 0, s>>>(T, E, k, R, nblk, hist, ded, assign, rep, maxrep,
-                                               rank_of, expert_offsets, rank_offsets, dedup);
+                                               rank_of, expert_offsets, rank_offsets, dedup,
+                                               ss_rank_offsets);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
   // 16 waves per permute block when blocks hold many pairs and the per-wave
@@ -310,6 +399,15 @@ hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const i
   else
     layout_permute_kernel<4><<<nblk, 4 * kWave, 9 * E * sizeof(int), s>>>(
         idx, T, E, k, bl.layout_tpb, hist, expert_offsets, pos, src);
+  err = hipGetLastError();
+  if (err != hipSuccess || !ss) return err;
+  // LDS: E + (1 + 2 WAVES) R ints; 16 waves while that stays small
+  if ((int64_t)bl.layout_tpb * k >= 1024 && E + 33 * R <= 12 * 1024)
+    layout_single_send_kernel<16><<<nblk, 16 * kWave, (E + 33 * R) * sizeof(int), s>>>(
+        idx, T, E, k, R, bl.layout_tpb, rank_of, ded, ss_rank_offsets, lead, ss_row, ss_token);
+  else
+    layout_single_send_kernel<4><<<nblk, 4 * kWave, (E + 9 * R) * sizeof(int), s>>>(
+        idx, T, E, k, R, bl.layout_tpb, rank_of, ded, ss_rank_offsets, lead, ss_row, ss_token);
   return hipGetLastError();
 }
 

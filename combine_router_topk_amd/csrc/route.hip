@@ -173,7 +173,7 @@ Blocking blocking_for(int T, int E, int R) {
 size_t workspace_bytes(int T, int E, int R) {
   const Blocking b = blocking_for(T, E, R);
   const size_t route = (size_t)b.route_nblk * E * sizeof(int32_t);
-  const size_t layout = (size_t)b.layout_nblk * (E + R) * sizeof(int32_t);
+  const size_t layout = ((size_t)b.layout_nblk * (E + R) + (size_t)T) * sizeof(int32_t);
   size_t n = route > layout ? route : layout;
   n = (n + 255) & ~(size_t)255;
   return n < 256 ? 256 : n;

@@ -51,10 +51,14 @@ __device__ __forceinline__ void row_team(int tpt, int& row, int& lane, int& stri
 // issued: for long rows with many copies (H = 7168, k = 8: 56 stores per
 // lane) this staggers the waves' store bursts and measured 7% faster
 // (1.63 vs 1.76 ms); for shorter rows it does not help.
-template <int NT, int U, bool ONE, bool SERIAL = false>
+//
+// With SS (single-send dispatch), pos is the token's single-send row per slot
+// and n_rows the buffer's row capacity; a row shared by several slots (the
+// same destination rank) is written once, by its first slot.
+template <int NT, int U, bool ONE, bool SERIAL = false, bool SS = false>
 __global__ __launch_bounds__(NT) void dispatch_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ send, int T,
-    int k, int cpr, int tpt) {
+    int k, int cpr, int tpt, int capacity = 0) {
   // Dynamic LDS is only allocated for a kernel that declares it; the launch
   // may reserve some here to cap how many blocks share a CU. Never accessed.
   extern __shared__ int occupancy_reserve[];
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(
   int t, lt, stride;
   row_team<NT, ONE>(tpt, t, lt, stride);
   if (t >= T) return;
-  const int n_rows = T * k;
+  const int n_rows = SS ? capacity : T * k;
   const u32x4* xr = x + (size_t)t * cpr;
   const int32_t* pr = pos + (size_t)t * k;
   for (int c0 = lt; c0 < cpr; c0 += stride * U) {
@@ -76,6 +80,11 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(
     for (int j = 0; j < k; ++j) {
       const int r = pr[j];
       if (static_cast<unsigned>(r) >= static_cast<unsigned>(n_rows)) continue;  // bad pos: skipped
+      if constexpr (SS) {
+        bool dup = false;
+        for (int jj = 0; jj < j; ++jj) dup |= (pr[jj] == r);
+        if (dup) continue;
+      }
       u32x4* dst = send + (size_t)r * cpr;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -215,6 +224,33 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
   }
 }
 
+// Receiver fan-out of single-send rows: send[p] = send_ss[ss_row[src[p]]],
+// one send row per block; rows whose source is out of range are skipped.
+template <int NT, int U>
+__global__ __launch_bounds__(NT) void expand_kernel(
+    const u32x4* __restrict__ send_ss, const int32_t* __restrict__ ss_row,
+    const int32_t* __restrict__ src, int capacity, u32x4* __restrict__ send, int n, int cpr) {
+  const int p = blockIdx.x;
+  const int sp = src[p];
+  const int q = static_cast<unsigned>(sp) < static_cast<unsigned>(n) ? ss_row[sp] : -1;
+  if (static_cast<unsigned>(q) >= static_cast<unsigned>(capacity)) return;
+  const u32x4* in = send_ss + (size_t)q * cpr;
+  u32x4* out = send + (size_t)p * cpr;
+  for (int c0 = threadIdx.x; c0 < cpr; c0 += NT * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * NT;
+      if (c < cpr) v[u] = __builtin_nontemporal_load(in + c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * NT;
+      if (c < cpr) __builtin_nontemporal_store(v[u], out + c);
+    }
+  }
+}
+
 // Rows of at least this many 16-byte chunks get a block each.
 constexpr int kOneRowChunks = 64;
 
@@ -300,6 +336,42 @@ hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T,
     else if (u == 7) dispatch_kernel<128, 7, true, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
     else dispatch_kernel<128, 8, true, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_single_send_dispatch(const void* x, const int32_t* ss_row, void* send_ss,
+                                       int ss_capacity, int T, int k, int H, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int cpr = H / 8;
+  const u32x4* xv = static_cast<const u32x4*>(x);
+  u32x4* sv = static_cast<u32x4*>(send_ss);
+  const size_t res = kDispatchLdsReserve;
+  const int cap = ss_capacity;
+  if (cpr < kOneRowChunks) {
+    const int tpt = threads_per_row(cpr);
+    const int per_blk = kRowThreads / tpt;
+    dispatch_kernel<kRowThreads, 1, false, false, true><<<(T + per_blk - 1) / per_blk, kRowThreads, res, s>>>(
+        xv, ss_row, sv, T, k, cpr, tpt, cap);
+  } else if (cpr <= 256) {
+    dispatch_kernel<kRowThreads, 1, true, false, true><<<T, kRowThreads, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
+  } else if (cpr <= 512) {
+    dispatch_kernel<kRowThreads, 2, true, false, true><<<T, kRowThreads, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
+  } else {
+    dispatch_kernel<128, 8, true, true, true><<<T, 128, 0, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_single_send_expand(const void* send_ss, const int32_t* ss_row,
+                                     const int32_t* src, int ss_capacity, void* send, int T, int k,
+                                     int H, hipStream_t s) {
+  const int n = T * k;
+  if (n == 0) return hipSuccess;
+  const int cpr = H / 8;
+  const u32x4* in = static_cast<const u32x4*>(send_ss);
+  u32x4* out = static_cast<u32x4*>(send);
+  if (cpr <= 256) expand_kernel<kRowThreads, 1><<<n, kRowThreads, 0, s>>>(in, ss_row, src, ss_capacity, out, n, cpr);
+  else expand_kernel<kRowThreads, 2><<<n, kRowThreads, 0, s>>>(in, ss_row, src, ss_capacity, out, n, cpr);
   return hipGetLastError();
 }
 

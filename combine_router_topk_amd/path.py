@@ -93,3 +93,38 @@ STEPS = (route, assign, layout, dispatch, standin, combine)
 def run(b: Buffers, stream=None) -> None:
     for step in STEPS:
         step(b, stream)
+
+
+@dataclass
+class SingleSend:
+    """Single-send buffers: one row per (token, destination rank). The row
+    capacity is T * min(k, R), the most distinct (token, rank) pairs a batch
+    can have, so no count has to be read back before the dispatch."""
+    ss_rank_offsets: torch.Tensor
+    ss_row: torch.Tensor
+    ss_token: torch.Tensor
+    send_ss: torch.Tensor
+
+
+def allocate_single_send(b: Buffers) -> SingleSend:
+    p, dev = b.p, b.idx.device
+    n, cap = p.T * p.k, p.T * min(p.k, p.R)
+    i32 = dict(dtype=torch.int32, device=dev)
+    return SingleSend(ss_rank_offsets=torch.empty(p.R + 1, **i32), ss_row=torch.empty(n, **i32),
+                      ss_token=torch.empty(n, **i32),
+                      send_ss=torch.empty(cap, p.H, dtype=b.send.dtype, device=dev))
+
+
+def layout_single_send(b: Buffers, ss: SingleSend, stream=None) -> None:
+    B.moe_layout_single_send(b.p, b.idx, b.assign, b.rep, b.maxrep, b.rank_of, b.expert_offsets,
+                             b.rank_offsets, b.pos, b.src, b.dedup, ss.ss_rank_offsets, ss.ss_row,
+                             ss.ss_token, b.ws, stream)
+
+
+def single_send_dispatch(b: Buffers, ss: SingleSend, stream=None) -> None:
+    B.moe_single_send_dispatch(b.p, b.x, ss.ss_row, ss.send_ss, stream)
+
+
+def single_send_expand(b: Buffers, ss: SingleSend, stream=None) -> None:
+    """Fills b.send from the single-send rows (what dispatch writes)."""
+    B.moe_single_send_expand(b.p, ss.send_ss, ss.ss_row, b.src, b.send, stream)

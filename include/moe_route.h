@@ -155,6 +155,49 @@ moe_status moe_layout(const moe_problem* p, const int32_t* idx, const int32_t* a
                       int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos,
                       int32_t* src, int32_t* dedup, void* ws, size_t ws_bytes, void* stream);
 
+/* Everything moe_layout computes, plus the single-send rows: one send row
+ * per (token, destination rank) instead of one per (token, slot), so a token
+ * goes to each virtual GPU once. [CORR] section "Two locality techniques"
+ * (a dispatcher that sends each token to a GPU once; with correlated expert
+ * placement it removes dispatched rows).
+ * Single-send rows are grouped by destination rank, inside a rank by token.
+ *   ss_rank_offsets i32 [R+1] (write) first single-send row of each rank;
+ *                   [R] = n_ss = sum(dedup), the number of rows
+ *   ss_row          i32 [T*k] (write) the single-send row carrying pair
+ *                   (t, j) at index t*k + j; the pairs of one token whose
+ *                   experts sit on the same rank share one row
+ *   ss_token        i32 [T*k] (write) token of each single-send row; entries
+ *                   from n_ss on are left untouched
+ * The other arguments are those of moe_layout. The workspace is the same
+ * size (moe_workspace_bytes).                                              */
+moe_status moe_layout_single_send(const moe_problem* p, const int32_t* idx, const int32_t* assign,
+                                  const int32_t* rep, int32_t maxrep, int32_t* rank_of,
+                                  int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos,
+                                  int32_t* src, int32_t* dedup, int32_t* ss_rank_offsets,
+                                  int32_t* ss_row, int32_t* ss_token, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Single-send dispatch: each token row x[t] is copied once to each distinct
+ * single-send row among ss_row[t*k .. t*k+k). [CORR] section "Two locality
+ * techniques".
+ *   x        16-bit [T, H] (read)   ss_row i32 [T*k] (read), from
+ *            moe_layout_single_send
+ *   send_ss  16-bit [ss_capacity, H] (write); ss_capacity >= n_ss rows
+ *            (rows at or beyond ss_capacity are skipped)                   */
+moe_status moe_single_send_dispatch(const moe_problem* p, const void* x, const int32_t* ss_row,
+                                    void* send_ss, int32_t ss_capacity, void* stream);
+
+/* Receiver-side fan-out of single-send rows to the expert-grouped layout:
+ * send[p] = send_ss[ss_row[src[p]]] for every p < T*k, which equals what
+ * moe_dispatch writes. [CORR] section "Two locality techniques" (each GPU
+ * receives a token once and serves every selected expert it holds).
+ *   send_ss 16-bit [ss_capacity, H] (read)   ss_row, src i32 [T*k] (read)
+ *   send    16-bit [T*k, H] (write); rows whose source row is out of range
+ *           are left untouched                                             */
+moe_status moe_single_send_expand(const moe_problem* p, const void* send_ss, const int32_t* ss_row,
+                                  const int32_t* src, int32_t ss_capacity, void* send,
+                                  void* stream);
+
 /* Row dispatch: send[pos[i]] = x[i / k] for every i < T*k, a bit copy.
  * [METRO] section "Work the 8-GPU payload example" (the dispatch payload is
  * token activation rows).

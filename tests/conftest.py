@@ -12,8 +12,12 @@ LIB = os.path.join(ROOT, "combine_router_topk_amd", "libmoe_route.so")
 
 # Tests load what is built; they build only when nothing is.
 if not os.path.exists(LIB):
-    from combine_router_topk_amd.build import build as _build
-    _build()
+    import importlib.util
+    _spec = importlib.util.spec_from_file_location(
+        "_moe_build", os.path.join(ROOT, "combine_router_topk_amd", "build.py"))
+    _mod = importlib.util.module_from_spec(_spec)
+    _spec.loader.exec_module(_mod)
+    _mod.build()
 
 
 def pytest_configure(config):
