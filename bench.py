@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--warm-cache", action="store_true", help="no cache flush before dispatch/combine")
+    ap.add_argument("--single-send-steps", type=int, default=20,
+                    help="timed passes of the single-send variant after the headline loop (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 30,
                     help="tokens in the oracle's CPU-baseline sample (0 = skip; default all)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -102,6 +104,49 @@ def cpu_baseline(w, seed: int, tokens: int, min_seconds: float):
             "routed_rows_per_s": round(reps * sub.T * sub.k / secs, 1)}
 
 
+def single_send_leg(P, w, b, flush, steps, ev, np, torch):
+    """The single-send variant on the same batch, timed after the headline
+    loop: its layout (the plain layout plus the single-send rows), the
+    dispatch of one row per (token, destination rank), and the receiver
+    fan-out back to the expert-grouped buffer, each cold-cache like the
+    headline. Algorithmic bytes: dispatch (T + n_ss) H b, fan-out
+    (n_ss + T k) H b (each single-send row read once, every expert row
+    written once)."""
+    ss = P.allocate_single_send(b)
+    marks = []
+    for i in range(steps + 2):
+        e = [ev() for _ in range(6)]
+        e[0].record()
+        P.layout_single_send(b, ss)
+        e[1].record()
+        if flush is not None:
+            flush.fill_(4.0)
+        e[2].record()
+        P.single_send_dispatch(b, ss)
+        e[3].record()
+        if flush is not None:
+            flush.fill_(5.0)
+        e[4].record()
+        P.single_send_expand(b, ss)
+        e[5].record()
+        if i >= 2:
+            marks.append(e)
+    torch.cuda.synchronize()
+    avg = lambda i: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks]))
+    lay_ms, dsp_ms, exp_ms = avg(0), avg(2), avg(4)
+    n_ss = int(ss.ss_rank_offsets[-1].item())
+    rb = w.H * 2
+    d_bytes = (w.T + n_ss) * rb
+    x_bytes = (n_ss + w.T * w.k) * rb
+    return {"rows": n_ss, "raw_rows": w.T * w.k, "rows_cut_frac": round(1 - n_ss / (w.T * w.k), 4),
+            "steps": steps,
+            "stage_ms": {"layout": round(lay_ms, 4), "dispatch": round(dsp_ms, 4),
+                         "expand": round(exp_ms, 4)},
+            "dispatch_GBps": round(d_bytes / (dsp_ms / 1e3) / 1e9, 1),
+            "expand_GBps": round(x_bytes / (exp_ms / 1e3) / 1e9, 1),
+            "dispatch_bytes": d_bytes, "expand_bytes": x_bytes}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -130,12 +175,17 @@ def main():
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    marks = []
+    marks, meta_marks = [], []
 
     def step(record: bool):
+        m0, m1, m2, m3 = ev(), ev(), ev(), ev()
+        m0.record()
         P.route(b)
+        m1.record()
         P.assign(b)
+        m2.record()
         P.layout(b)
+        m3.record()
         if flush is not None:
             flush.fill_(1.0)
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
@@ -150,6 +200,7 @@ def main():
         e3.record()
         if record:
             marks.append((e0, e1, e2, e3))
+            meta_marks.append((m0, m1, m2, m3))
 
     for _ in range(args.warmup):
         step(False)
@@ -160,6 +211,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
+    meta_ms = {name: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in meta_marks]))
+               for i, name in enumerate(("route", "assign", "layout"))}
     disp_ms = float(np.mean([a.elapsed_time(b_) for a, b_, _, _ in marks]))
     comb_ms = float(np.mean([c.elapsed_time(d) for _, _, c, d in marks]))
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -205,7 +258,8 @@ def main():
                    "cache": "warm" if flush is None else "cold: 1 GiB fill before dispatch and before combine"},
         "frac_of_peak": round(value / PEAK_GBPS, 4),
         "routed_rows_per_s": round(w.T * w.k / dc_s, 1),
-        "stage_ms": {"dispatch": round(disp_ms, 4), "combine": round(comb_ms, 4)},
+        "stage_ms": {**{k_: round(v_, 4) for k_, v_ in meta_ms.items()},
+                     "dispatch": round(disp_ms, 4), "combine": round(comb_ms, 4)},
         "dedup_rows": int(b.dedup.sum().item()),
         "raw_rows": w.T * w.k,
         "max_active_experts": int(b.active.max().item()),
@@ -214,6 +268,8 @@ def main():
                      "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": traffic},
     }
+    if args.single_send_steps > 0:
+        res["single_send"] = single_send_leg(P, w, b, flush, args.single_send_steps, ev, np, torch)
     if args.cpu_tokens > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_tokens, args.cpu_seconds)
     print(json.dumps(res), flush=True)

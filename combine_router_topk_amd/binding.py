@@ -63,7 +63,7 @@ def _load() -> ctypes.CDLL:
         "moe_layout_single_send": (i32, [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, sz, vp]),
         "moe_single_send_dispatch": (i32, [P, vp, vp, vp, i32, vp]),
-        "moe_single_send_expand": (i32, [P, vp, vp, vp, i32, vp, vp]),
+        "moe_single_send_expand": (i32, [P, vp, vp, vp, vp, vp, i32, vp, vp]),
         "moe_dispatch": (i32, [P, vp, vp, vp, vp]),
         "moe_expert_standin": (i32, [P, vp, vp, vp, vp, vp]),
         "moe_combine": (i32, [P, vp, vp, vp, vp, vp]),
@@ -191,13 +191,17 @@ def moe_single_send_dispatch(p: Problem, x, ss_row, send_ss, stream=None) -> Non
                                          _stream(stream)), "moe_single_send_dispatch")
 
 
-def moe_single_send_expand(p: Problem, send_ss, ss_row, src, send, stream=None) -> None:
+def moe_single_send_expand(p: Problem, send_ss, ss_rank_offsets, ss_token, ss_row, pos, send,
+                           stream=None) -> None:
+    """send_ss holds the single-send rows; its row count is the capacity."""
     act = _TORCH_ACT.get(p.act_dtype)
     n = p.T * p.k
     cap = send_ss.shape[0]
     _check(_lib.moe_single_send_expand(ctypes.byref(p), _ptr(send_ss, act, cap * p.H, "send_ss"),
+                                       _ptr(ss_rank_offsets, torch.int32, p.R + 1, "ss_rank_offsets"),
+                                       _ptr(ss_token, torch.int32, min(cap, n), "ss_token"),
                                        _ptr(ss_row, torch.int32, n, "ss_row"),
-                                       _ptr(src, torch.int32, n, "src"), cap,
+                                       _ptr(pos, torch.int32, n, "pos"), cap,
                                        _ptr(send, act, n * p.H, "send"), _stream(stream)),
            "moe_single_send_expand")
 

@@ -206,20 +206,24 @@ moe_status moe_single_send_dispatch(const moe_problem* p, const void* x, const i
                     fn);
 }
 
-moe_status moe_single_send_expand(const moe_problem* p, const void* send_ss, const int32_t* ss_row,
-                                  const int32_t* src, int32_t ss_capacity, void* send,
-                                  void* stream) {
+moe_status moe_single_send_expand(const moe_problem* p, const void* send_ss,
+                                  const int32_t* ss_rank_offsets, const int32_t* ss_token,
+                                  const int32_t* ss_row, const int32_t* pos, int32_t ss_capacity,
+                                  void* send, void* stream) {
   const char* fn = "moe_single_send_expand";
   CHECK(check_problem(p, fn));
   if (ss_capacity < 0) return fail(MOE_ERR_INVALID_ARG, "%s: ss_capacity=%d < 0", fn, ss_capacity);
-  if (p->T == 0) return MOE_OK;
+  if (p->T == 0 || ss_capacity == 0) return MOE_OK;
   CHECK(need(send_ss, 16, fn, "send_ss"));
+  CHECK(need(ss_rank_offsets, 4, fn, "ss_rank_offsets"));
+  CHECK(need(ss_token, 4, fn, "ss_token"));
   CHECK(need(ss_row, 4, fn, "ss_row"));
-  CHECK(need(src, 4, fn, "src"));
+  CHECK(need(pos, 4, fn, "pos"));
   CHECK(need(send, 16, fn, "send"));
   clear_stale_error();
-  return hip_status(moe::launch_single_send_expand(send_ss, ss_row, src, ss_capacity, send, p->T,
-                                                   p->k, p->H, static_cast<hipStream_t>(stream)),
+  return hip_status(moe::launch_single_send_expand(send_ss, ss_rank_offsets, ss_token, ss_row, pos,
+                                                   ss_capacity, send, p->T, p->k, p->R, p->H,
+                                                   static_cast<hipStream_t>(stream)),
                     fn);
 }
 

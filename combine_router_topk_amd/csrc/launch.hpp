@@ -38,9 +38,10 @@ hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const i
 hipError_t launch_single_send_dispatch(const void* x, const int32_t* ss_row, void* send_ss,
                                        int ss_capacity, int T, int k, int H, hipStream_t s);
 
-hipError_t launch_single_send_expand(const void* send_ss, const int32_t* ss_row,
-                                     const int32_t* src, int ss_capacity, void* send, int T, int k,
-                                     int H, hipStream_t s);
+hipError_t launch_single_send_expand(const void* send_ss, const int32_t* ss_rank_offsets,
+                                     const int32_t* ss_token, const int32_t* ss_row,
+                                     const int32_t* pos, int ss_capacity, void* send, int T, int k,
+                                     int R, int H, hipStream_t s);
 
 hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T, int k, int H,
                            hipStream_t s);

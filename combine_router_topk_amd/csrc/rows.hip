@@ -224,18 +224,24 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
   }
 }
 
-// Receiver fan-out of single-send rows: send[p] = send_ss[ss_row[src[p]]],
-// one send row per block; rows whose source is out of range are skipped.
+// Receiver fan-out of single-send rows: each single-send row q (token t =
+// ss_token[q]) is read once and written to the expert rows pos[t*k + j] of
+// every slot j that it carries (ss_row[t*k + j] == q). One row per block, so
+// the token, its slots' rows and their destinations are uniform (scalar
+// loads). Rows at or beyond n_ss = ss_rank_offsets[R] exit at once.
 template <int NT, int U>
-__global__ __launch_bounds__(NT) void expand_kernel(
-    const u32x4* __restrict__ send_ss, const int32_t* __restrict__ ss_row,
-    const int32_t* __restrict__ src, int capacity, u32x4* __restrict__ send, int n, int cpr) {
-  const int p = blockIdx.x;
-  const int sp = src[p];
-  const int q = static_cast<unsigned>(sp) < static_cast<unsigned>(n) ? ss_row[sp] : -1;
-  if (static_cast<unsigned>(q) >= static_cast<unsigned>(capacity)) return;
+__global__ __launch_bounds__(NT) void fanout_kernel(
+    const u32x4* __restrict__ send_ss, const int32_t* __restrict__ n_ss_ptr,
+    const int32_t* __restrict__ ss_token, const int32_t* __restrict__ ss_row,
+    const int32_t* __restrict__ pos, u32x4* __restrict__ send, int T, int k, int cpr) {
+  const int q = blockIdx.x;
+  if (q >= *n_ss_ptr) return;
+  const int t = ss_token[q];
+  if (static_cast<unsigned>(t) >= static_cast<unsigned>(T)) return;
+  const int n_rows = T * k;
+  const int32_t* sr = ss_row + (size_t)t * k;
+  const int32_t* pr = pos + (size_t)t * k;
   const u32x4* in = send_ss + (size_t)q * cpr;
-  u32x4* out = send + (size_t)p * cpr;
   for (int c0 = threadIdx.x; c0 < cpr; c0 += NT * U) {
     u32x4 v[U];
 #pragma unroll
@@ -243,10 +249,15 @@ __global__ __launch_bounds__(NT) void expand_kernel(
       const int c = c0 + u * NT;
       if (c < cpr) v[u] = __builtin_nontemporal_load(in + c);
     }
+    for (int j = 0; j < k; ++j) {
+      const int r = pr[j];
+      if (sr[j] != q || static_cast<unsigned>(r) >= static_cast<unsigned>(n_rows)) continue;
+      u32x4* dst = send + (size_t)r * cpr;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * NT;
-      if (c < cpr) __builtin_nontemporal_store(v[u], out + c);
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * NT;
+        if (c < cpr) __builtin_nontemporal_store(v[u], dst + c);
+      }
     }
   }
 }
@@ -362,16 +373,21 @@ hipError_t launch_single_send_dispatch(const void* x, const int32_t* ss_row, voi
   return hipGetLastError();
 }
 
-hipError_t launch_single_send_expand(const void* send_ss, const int32_t* ss_row,
-                                     const int32_t* src, int ss_capacity, void* send, int T, int k,
-                                     int H, hipStream_t s) {
-  const int n = T * k;
-  if (n == 0) return hipSuccess;
+hipError_t launch_single_send_expand(const void* send_ss, const int32_t* ss_rank_offsets,
+                                     const int32_t* ss_token, const int32_t* ss_row,
+                                     const int32_t* pos, int ss_capacity, void* send, int T, int k,
+                                     int R, int H, hipStream_t s) {
+  if (T == 0 || ss_capacity == 0) return hipSuccess;
   const int cpr = H / 8;
   const u32x4* in = static_cast<const u32x4*>(send_ss);
   u32x4* out = static_cast<u32x4*>(send);
-  if (cpr <= 256) expand_kernel<kRowThreads, 1><<<n, kRowThreads, 0, s>>>(in, ss_row, src, ss_capacity, out, n, cpr);
-  else expand_kernel<kRowThreads, 2><<<n, kRowThreads, 0, s>>>(in, ss_row, src, ss_capacity, out, n, cpr);
+  const int32_t* n_ss = ss_rank_offsets + R;
+  if (cpr <= 256)
+    fanout_kernel<kRowThreads, 1><<<ss_capacity, kRowThreads, 0, s>>>(in, n_ss, ss_token, ss_row,
+                                                                     pos, out, T, k, cpr);
+  else
+    fanout_kernel<kRowThreads, 2><<<ss_capacity, kRowThreads, 0, s>>>(in, n_ss, ss_token, ss_row,
+                                                                     pos, out, T, k, cpr);
   return hipGetLastError();
 }
 

@@ -127,4 +127,5 @@ def single_send_dispatch(b: Buffers, ss: SingleSend, stream=None) -> None:
 
 def single_send_expand(b: Buffers, ss: SingleSend, stream=None) -> None:
     """Fills b.send from the single-send rows (what dispatch writes)."""
-    B.moe_single_send_expand(b.p, ss.send_ss, ss.ss_row, b.src, b.send, stream)
+    B.moe_single_send_expand(b.p, ss.send_ss, ss.ss_rank_offsets, ss.ss_token, ss.ss_row, b.pos,
+                             b.send, stream)

@@ -188,15 +188,22 @@ moe_status moe_single_send_dispatch(const moe_problem* p, const void* x, const i
                                     void* send_ss, int32_t ss_capacity, void* stream);
 
 /* Receiver-side fan-out of single-send rows to the expert-grouped layout:
- * send[p] = send_ss[ss_row[src[p]]] for every p < T*k, which equals what
+ * send[pos[i]] = send_ss[ss_row[i]] for every pair i < T*k, which equals what
  * moe_dispatch writes. [CORR] section "Two locality techniques" (each GPU
- * receives a token once and serves every selected expert it holds).
- *   send_ss 16-bit [ss_capacity, H] (read)   ss_row, src i32 [T*k] (read)
- *   send    16-bit [T*k, H] (write); rows whose source row is out of range
- *           are left untouched                                             */
-moe_status moe_single_send_expand(const moe_problem* p, const void* send_ss, const int32_t* ss_row,
-                                  const int32_t* src, int32_t ss_capacity, void* send,
-                                  void* stream);
+ * receives a token once and serves every selected expert it holds). Each
+ * single-send row is read once and written to the expert rows of all the
+ * slots it carries.
+ *   send_ss          16-bit [ss_capacity, H] (read)
+ *   ss_rank_offsets  i32 [R+1] (read; [R] = n_ss)   ss_token i32 [n_ss] (read)
+ *   ss_row, pos      i32 [T*k] (read), from moe_layout_single_send
+ *   send             16-bit [T*k, H] (write)
+ * Single-send rows at or beyond min(n_ss, ss_capacity), and out-of-range
+ * tokens or positions, are skipped: their destination rows are left
+ * untouched.                                                               */
+moe_status moe_single_send_expand(const moe_problem* p, const void* send_ss,
+                                  const int32_t* ss_rank_offsets, const int32_t* ss_token,
+                                  const int32_t* ss_row, const int32_t* pos, int32_t ss_capacity,
+                                  void* send, void* stream);
 
 /* Row dispatch: send[pos[i]] = x[i / k] for every i < T*k, a bit copy.
  * [METRO] section "Work the 8-GPU payload example" (the dispatch payload is

@@ -33,7 +33,8 @@ def run_single_send(w, logits, x, rep, flags=0, capacity=None):
     P.single_send_dispatch(b, ss)
     expanded = torch.empty_like(b.send)
     expanded.view(torch.int16).fill_(SENTINEL)
-    B.moe_single_send_expand(p, ss.send_ss, ss.ss_row, b.src, expanded)
+    B.moe_single_send_expand(p, ss.send_ss, ss.ss_rank_offsets, ss.ss_token, ss.ss_row, b.pos,
+                             expanded)
     torch.cuda.synchronize()
     return b, ss, expanded
 
@@ -68,6 +69,13 @@ def check_single_send(w, b, ss, expanded, ref, capacity=None):
         # fan-out reproduces the plain dispatch exactly
         bad = rows_equal_chunked(expanded, lambda r0, r1: b.send[r0:r1], T * k)
         assert bad is None, f"expand rows from {bad}"
+    else:
+        # rows carried by a single-send row below the capacity are filled,
+        # the others untouched
+        carried = torch.from_numpy(want_row[ref["src"]] < cap).to(expanded.device)
+        got, want = expanded.view(torch.int16), b.send.view(torch.int16)
+        assert torch.equal(got[carried], want[carried]), "expand rows below the capacity"
+        assert bool((got[~carried] == SENTINEL).all()), "expand rows past the capacity written"
 
 
 SMALL = [
