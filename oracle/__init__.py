@@ -26,3 +26,4 @@ from .bytes_model import (allgather_bytes_per_gpu, alltoall_bytes_per_gpu,  # no
 from .pipeline import route_and_layout, rows_for  # noqa: F401
 from .single_send import (single_send_dispatch, single_send_expand,  # noqa: F401
                           single_send_layout)
+from .backward import combine_backward_dw, combine_backward_dy, dispatch_backward  # noqa: F401
