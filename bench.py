@@ -9,6 +9,11 @@ combine. The headline is dispatch+combine GB/s of algorithmic bytes,
 are flushed (a 1 GiB fill) before the dispatch and before the combine, outside
 their event brackets, so both read from HBM.
 
+After the headline loop, and outside it, the same batch also times the
+single-send variant (layout, one-row-per-rank dispatch, receiver fan-out) and
+the backward of the dispatch and the combine; each is reported in its own
+object of the JSON line.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line.
 """
@@ -41,6 +46,8 @@ def parse():
     ap.add_argument("--warm-cache", action="store_true", help="no cache flush before dispatch/combine")
     ap.add_argument("--single-send-steps", type=int, default=20,
                     help="timed passes of the single-send variant after the headline loop (0 = skip)")
+    ap.add_argument("--backward-steps", type=int, default=20,
+                    help="timed passes of the dispatch/combine backward after the headline loop (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 30,
                     help="tokens in the oracle's CPU-baseline sample (0 = skip; default all)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -145,6 +152,47 @@ def single_send_leg(P, w, b, flush, steps, ev, np, torch):
             "dispatch_GBps": round(d_bytes / (dsp_ms / 1e3) / 1e9, 1),
             "expand_GBps": round(x_bytes / (exp_ms / 1e3) / 1e9, 1),
             "dispatch_bytes": d_bytes, "expand_bytes": x_bytes}
+
+
+def backward_leg(B, w, b, flush, steps, ev, np, torch, synth, seed):
+    """The backward of the combine (dy and dw in one kernel) and of the
+    dispatch (dx) on the same batch, each cold-cache, timed after the
+    headline loop. Algorithmic bytes: combine backward (1 + 2k) T H b (dout
+    read once, y read and dy written per slot), dispatch backward
+    (1 + k) T H b; the 4-8 bytes per slot of pos, w and dw are left out, as in
+    the forward."""
+    dout = synth.make_grad(w, seed, w.T)
+    tdt = b.x.dtype
+    g = torch.from_numpy(dout.view(np.int16)).view(tdt).to(b.x.device)
+    dy = torch.empty_like(b.y)
+    dw = torch.empty(w.T * w.k, dtype=torch.float32, device=b.x.device)
+    dx = torch.empty_like(b.x)
+    marks = []
+    for i in range(steps + 2):
+        e = [ev() for _ in range(4)]
+        if flush is not None:
+            flush.fill_(6.0)
+        e[0].record()
+        B.moe_combine_backward(b.p, g, b.y, b.pos, b.w, dy, dw)
+        e[1].record()
+        if flush is not None:
+            flush.fill_(7.0)
+        e[2].record()
+        B.moe_dispatch_backward(b.p, dy, b.pos, dx)
+        e[3].record()
+        if i >= 2:
+            marks.append(e)
+    torch.cuda.synchronize()
+    cb_ms = float(np.mean([m[0].elapsed_time(m[1]) for m in marks]))
+    db_ms = float(np.mean([m[2].elapsed_time(m[3]) for m in marks]))
+    rb = w.H * 2
+    cb_bytes = (1 + 2 * w.k) * w.T * rb
+    db_bytes = (1 + w.k) * w.T * rb
+    return {"steps": steps,
+            "stage_ms": {"combine_backward": round(cb_ms, 4), "dispatch_backward": round(db_ms, 4)},
+            "combine_backward_GBps": round(cb_bytes / (cb_ms / 1e3) / 1e9, 1),
+            "dispatch_backward_GBps": round(db_bytes / (db_ms / 1e3) / 1e9, 1),
+            "combine_backward_bytes": cb_bytes, "dispatch_backward_bytes": db_bytes}
 
 
 def main():
@@ -270,6 +318,9 @@ def main():
     }
     if args.single_send_steps > 0:
         res["single_send"] = single_send_leg(P, w, b, flush, args.single_send_steps, ev, np, torch)
+    if args.backward_steps > 0:
+        res["backward"] = backward_leg(B, w, b, flush, args.backward_steps, ev, np, torch, synth,
+                                       args.seed)
     if args.cpu_tokens > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_tokens, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -10,6 +10,7 @@ libmoe_route.so and fails if it has not been built.
 """
 from .binding import (MOE_BF16, MOE_F16, MOE_FLAG_GREEDY_ID_ORDER, MOE_FLAG_OUT_F32,  # noqa: F401
                       MoeError, Problem, make_problem, moe_assign_replicas, moe_combine,
+                      moe_combine_backward, moe_dispatch_backward,
                       moe_dispatch, moe_expert_standin, moe_last_error, moe_layout,
                       moe_layout_single_send, moe_route, moe_single_send_dispatch,
                       moe_single_send_expand, moe_status_string, moe_version,

@@ -25,7 +25,7 @@ MOE_FLAG_OUT_F32 = 1 << 1
 EXPORTED = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
             "moe_route", "moe_assign_replicas", "moe_layout", "moe_layout_single_send",
             "moe_single_send_dispatch", "moe_single_send_expand", "moe_dispatch",
-            "moe_expert_standin", "moe_combine")
+            "moe_expert_standin", "moe_combine", "moe_combine_backward", "moe_dispatch_backward")
 
 _TORCH_ACT = {MOE_F16: torch.float16, MOE_BF16: torch.bfloat16}
 
@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
         "moe_dispatch": (i32, [P, vp, vp, vp, vp]),
         "moe_expert_standin": (i32, [P, vp, vp, vp, vp, vp]),
         "moe_combine": (i32, [P, vp, vp, vp, vp, vp]),
+        "moe_combine_backward": (i32, [P, vp, vp, vp, vp, vp, vp, vp]),
+        "moe_dispatch_backward": (i32, [P, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -230,3 +232,25 @@ def moe_combine(p: Problem, y, pos, w, out, stream=None) -> None:
     _check(_lib.moe_combine(ctypes.byref(p), _ptr(y, act, n * p.H, "y"),
                             _ptr(pos, torch.int32, n, "pos"), _ptr(w, torch.float32, n, "w"),
                             _ptr(out, out_dt, p.T * p.H, "out"), _stream(stream)), "moe_combine")
+
+
+def moe_combine_backward(p: Problem, dout, y, pos, w, dy, dw, stream=None) -> None:
+    """dy and/or dw (either may be None); y may be None without dw and w
+    without dy."""
+    act = _TORCH_ACT.get(p.act_dtype)
+    n = p.T * p.k
+    _check(_lib.moe_combine_backward(ctypes.byref(p), _ptr(dout, act, p.T * p.H, "dout"),
+                                     _ptr(y, act, n * p.H, "y"), _ptr(pos, torch.int32, n, "pos"),
+                                     _ptr(w, torch.float32, n, "w"), _ptr(dy, act, n * p.H, "dy"),
+                                     _ptr(dw, torch.float32, n, "dw"), _stream(stream)),
+           "moe_combine_backward")
+
+
+def moe_dispatch_backward(p: Problem, dsend, pos, dx, stream=None) -> None:
+    act = _TORCH_ACT.get(p.act_dtype)
+    out_dt = torch.float32 if p.flags & MOE_FLAG_OUT_F32 else act
+    n = p.T * p.k
+    _check(_lib.moe_dispatch_backward(ctypes.byref(p), _ptr(dsend, act, n * p.H, "dsend"),
+                                      _ptr(pos, torch.int32, n, "pos"),
+                                      _ptr(dx, out_dt, p.T * p.H, "dx"), _stream(stream)),
+           "moe_dispatch_backward")

@@ -272,4 +272,42 @@ moe_status moe_combine(const moe_problem* p, const void* y, const int32_t* pos, 
                     fn);
 }
 
+moe_status moe_combine_backward(const moe_problem* p, const void* dout, const void* y,
+                                const int32_t* pos, const float* w, void* dy, float* dw,
+                                void* stream) {
+  const char* fn = "moe_combine_backward";
+  CHECK(check_problem(p, fn));
+  if (p->T == 0) return MOE_OK;
+  if (dy == nullptr && dw == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: dy and dw are both NULL", fn);
+  CHECK(need(dout, 16, fn, "dout"));
+  CHECK(need(pos, 4, fn, "pos"));
+  if (dy != nullptr) {
+    CHECK(need(w, 4, fn, "w"));
+    CHECK(need(dy, 16, fn, "dy"));
+  }
+  if (dw != nullptr) {
+    CHECK(need(y, 16, fn, "y"));
+    CHECK(need(dw, 4, fn, "dw"));
+  }
+  clear_stale_error();
+  return hip_status(moe::launch_combine_backward(dout, y, pos, w, dy, dw, p->T, p->k, p->H,
+                                                 p->act_dtype, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+moe_status moe_dispatch_backward(const moe_problem* p, const void* dsend, const int32_t* pos,
+                                 void* dx, void* stream) {
+  const char* fn = "moe_dispatch_backward";
+  CHECK(check_problem(p, fn));
+  if (p->T == 0) return MOE_OK;
+  CHECK(need(dsend, 16, fn, "dsend"));
+  CHECK(need(pos, 4, fn, "pos"));
+  CHECK(need(dx, 16, fn, "dx"));
+  clear_stale_error();
+  return hip_status(moe::launch_dispatch_backward(dsend, pos, dx, p->T, p->k, p->H, p->act_dtype,
+                                                  (p->flags & MOE_FLAG_OUT_F32) != 0,
+                                                  static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

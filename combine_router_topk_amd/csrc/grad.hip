@@ -1,0 +1,293 @@
+// Backward of the combine and of the dispatch.
+//
+// News summary of correlated expert placement and token shuffling, section
+// "Why communication is the target": each MoE layer dispatches tokens and
+// combines results in the backward pass as in the forward. Differentiating
+// the forward maps out[t] = sum_j w[t,j] y[pos[t*k+j]] and
+// send[pos[i]] = x[i/k] gives
+//   dy[pos[t*k+j]] = w[t,j] * dout[t]          (a dispatch-shaped weighted scatter)
+//   dw[t,j]        = <y[pos[t*k+j]], dout[t]>  (row dot products)
+//   dx[t]          = sum_j dsend[pos[t*k+j]]   (a combine-shaped gather-sum)
+//
+// Both kernels give each token a team of lanes (a whole 256-thread block for
+// rows of 64 chunks or more, else 16-64 lanes inside one wave) that walks the
+// token's row in 16-byte chunks, so every gradient row is read once and
+// every output row written once: (1 + 2k) T H b bytes for the combine
+// backward with both outputs, (1 + k) T H b for the dispatch backward.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGradThreads = 256;
+constexpr int kGradWaves = kGradThreads / kWave;
+constexpr int kGradOneRowChunks = 64;  // rows of at least this many chunks get a block each
+
+__device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
+__device__ __forceinline__ u32x4 as_vec(uint4 v) { return u32x4{v.x, v.y, v.z, v.w}; }
+
+// The token a lane works on, its index inside the token's team, and the
+// team's width (the chunk stride).
+template <bool ONE>
+__device__ __forceinline__ void grad_team(int tpt, int& t, int& lt, int& stride) {
+  if constexpr (ONE) {
+    t = blockIdx.x;
+    lt = threadIdx.x;
+    stride = kGradThreads;
+  } else {
+    t = blockIdx.x * (kGradThreads / tpt) + threadIdx.x / tpt;
+    lt = threadIdx.x % tpt;
+    stride = tpt;
+  }
+}
+
+// dy and dw for one token per team. dy (nullable) = rne16(fp32(w * dout));
+// dw (nullable) = fp32 dot products, summed per lane over its chunks in
+// order, then over the team (a butterfly inside the wave, then the block's
+// waves in order). Slots whose pos is out of range write no dy row and a dw
+// of 0. dy may alias y: every chunk of y is read before the same lane
+// writes that chunk of dy.
+template <int ACT, int KMAX, bool ONE>
+__global__ __launch_bounds__(kGradThreads) void combine_backward_kernel(
+    const u32x4* __restrict__ dout, const u32x4* y, const int32_t* __restrict__ pos,
+    const float* __restrict__ w, u32x4* dy, float* __restrict__ dw, int T, int k, int cpr,
+    int tpt) {
+  __shared__ float s_part[kGradWaves][KMAX];
+  int t, lt, stride;
+  grad_team<ONE>(tpt, t, lt, stride);
+  const bool live = t < T;
+  if (ONE && !live) return;  // uniform over the block
+  const bool do_dy = dy != nullptr;
+  const bool do_dw = dw != nullptr;
+  const int n_rows = T * k;
+  size_t row[KMAX];
+  bool ok[KMAX];
+  float wt[KMAX];
+  float part[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    part[j] = 0.0f;
+    ok[j] = false;
+    row[j] = 0;
+    wt[j] = 0.0f;
+    if (live && j < k) {
+      const int r = pos[(size_t)t * k + j];
+      ok[j] = static_cast<unsigned>(r) < static_cast<unsigned>(n_rows);
+      row[j] = ok[j] ? (size_t)r * cpr : 0;
+      wt[j] = w != nullptr ? w[(size_t)t * k + j] : 0.0f;
+    }
+  }
+  if (live) {
+    const u32x4* g_row = dout + (size_t)t * cpr;
+    for (int c = lt; c < cpr; c += stride) {
+      float g[8];
+      unpack8<ACT>(as_uint4(__builtin_nontemporal_load(g_row + c)), g);
+      if (do_dw) {
+        u32x4 v[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (j < k && ok[j]) v[j] = __builtin_nontemporal_load(y + row[j] + c);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (j < k && ok[j]) {
+            float f[8];
+            unpack8<ACT>(as_uint4(v[j]), f);
+            float s = part[j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s = fmaf(f[i], g[i], s);
+            part[j] = s;
+          }
+        }
+      }
+      if (do_dy) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (j < k && ok[j]) {
+            float p[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) p[i] = keep_f32(wt[j] * g[i]);  // fp32 product, then one rounding
+            __builtin_nontemporal_store(as_vec(pack8<ACT>(p)), dy + row[j] + c);
+          }
+        }
+      }
+    }
+  }
+  if (!do_dw) return;  // uniform: a kernel argument
+  // team sum of each slot's partial dot product
+  const int width = ONE ? kWave : tpt;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      float s = part[j];
+      for (int off = width / 2; off > 0; off /= 2) s += __shfl_xor(s, off, width);
+      part[j] = s;
+    }
+  }
+  if constexpr (ONE) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k) s_part[wave][j] = part[j];
+    }
+    __syncthreads();
+    if (threadIdx.x < k) {
+      const int j = threadIdx.x;
+      float s = 0.0f;
+#pragma unroll
+      for (int v = 0; v < kGradWaves; ++v) s += s_part[v][j];
+      const int r = pos[(size_t)t * k + j];
+      dw[(size_t)t * k + j] = static_cast<unsigned>(r) < static_cast<unsigned>(n_rows) ? s : 0.0f;
+    }
+  } else {
+    if (live && lt == 0) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k) dw[(size_t)t * k + j] = ok[j] ? part[j] : 0.0f;
+    }
+  }
+}
+
+template <int ACT, bool OUT_F32>
+__device__ __forceinline__ void grad_store(void* __restrict__ out, size_t chunk, const float (&acc)[8]) {
+  if constexpr (OUT_F32) {
+    f32x4* o = reinterpret_cast<f32x4*>(out) + chunk * 2;
+    __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, o);
+    __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, o + 1);
+  } else {
+    __builtin_nontemporal_store(as_vec(pack8<ACT>(acc)), reinterpret_cast<u32x4*>(out) + chunk);
+  }
+}
+
+// dx[t] = sum_j (ascending) dsend[pos[t*k+j]] in fp32, stored in the
+// activation format (one rounding) or as fp32. The k row loads of a chunk
+// position are issued before the sums. Slots whose pos is out of range add
+// nothing.
+template <int ACT, int KMAX, bool OUT_F32, bool ONE>
+__global__ __launch_bounds__(kGradThreads) void dispatch_backward_kernel(
+    const u32x4* __restrict__ dsend, const int32_t* __restrict__ pos, void* __restrict__ dx, int T,
+    int k, int cpr, int tpt) {
+  int t, lt, stride;
+  grad_team<ONE>(tpt, t, lt, stride);
+  if (t >= T) return;
+  const int n_rows = T * k;
+  size_t row[KMAX];
+  bool ok[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    ok[j] = false;
+    row[j] = 0;
+    if (j < k) {
+      const int r = pos[(size_t)t * k + j];
+      ok[j] = static_cast<unsigned>(r) < static_cast<unsigned>(n_rows);
+      row[j] = ok[j] ? (size_t)r * cpr : 0;
+    }
+  }
+  for (int c = lt; c < cpr; c += stride) {
+    u32x4 v[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k && ok[j]) v[j] = __builtin_nontemporal_load(dsend + row[j] + c);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k && ok[j]) {
+        float f[8];
+        unpack8<ACT>(as_uint4(v[j]), f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += f[i];
+      }
+    }
+    grad_store<ACT, OUT_F32>(dx, (size_t)t * cpr + c, acc);
+  }
+}
+
+int grad_threads_per_row(int cpr) {
+  int tpt = 16;
+  while (tpt < cpr && tpt < kWave) tpt *= 2;
+  return tpt;
+}
+
+template <int ACT, int KMAX>
+hipError_t launch_cb(const u32x4* dout, const u32x4* y, const int32_t* pos, const float* w,
+                     u32x4* dy, float* dw, int T, int k, int cpr, hipStream_t s) {
+  if (cpr >= kGradOneRowChunks) {
+    combine_backward_kernel<ACT, KMAX, true><<<T, kGradThreads, 0, s>>>(dout, y, pos, w, dy, dw, T,
+                                                                       k, cpr, kGradThreads);
+  } else {
+    const int tpt = grad_threads_per_row(cpr);
+    const int per_blk = kGradThreads / tpt;
+    combine_backward_kernel<ACT, KMAX, false><<<(T + per_blk - 1) / per_blk, kGradThreads, 0, s>>>(
+        dout, y, pos, w, dy, dw, T, k, cpr, tpt);
+  }
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_cb_k(const u32x4* dout, const u32x4* y, const int32_t* pos, const float* w,
+                       u32x4* dy, float* dw, int T, int k, int cpr, hipStream_t s) {
+  if (k <= 2) return launch_cb<ACT, 2>(dout, y, pos, w, dy, dw, T, k, cpr, s);
+  if (k <= 4) return launch_cb<ACT, 4>(dout, y, pos, w, dy, dw, T, k, cpr, s);
+  if (k <= 8) return launch_cb<ACT, 8>(dout, y, pos, w, dy, dw, T, k, cpr, s);
+  return launch_cb<ACT, 16>(dout, y, pos, w, dy, dw, T, k, cpr, s);
+}
+
+template <int ACT, int KMAX, bool OUT_F32>
+hipError_t launch_db(const u32x4* dsend, const int32_t* pos, void* dx, int T, int k, int cpr,
+                     hipStream_t s) {
+  if (cpr >= kGradOneRowChunks) {
+    dispatch_backward_kernel<ACT, KMAX, OUT_F32, true><<<T, kGradThreads, 0, s>>>(
+        dsend, pos, dx, T, k, cpr, kGradThreads);
+  } else {
+    const int tpt = grad_threads_per_row(cpr);
+    const int per_blk = kGradThreads / tpt;
+    dispatch_backward_kernel<ACT, KMAX, OUT_F32, false>
+        <<<(T + per_blk - 1) / per_blk, kGradThreads, 0, s>>>(dsend, pos, dx, T, k, cpr, tpt);
+  }
+  return hipGetLastError();
+}
+
+template <int ACT, bool OUT_F32>
+hipError_t launch_db_k(const u32x4* dsend, const int32_t* pos, void* dx, int T, int k, int cpr,
+                       hipStream_t s) {
+  if (k <= 2) return launch_db<ACT, 2, OUT_F32>(dsend, pos, dx, T, k, cpr, s);
+  if (k <= 4) return launch_db<ACT, 4, OUT_F32>(dsend, pos, dx, T, k, cpr, s);
+  if (k <= 8) return launch_db<ACT, 8, OUT_F32>(dsend, pos, dx, T, k, cpr, s);
+  return launch_db<ACT, 16, OUT_F32>(dsend, pos, dx, T, k, cpr, s);
+}
+
+}  // namespace
+
+hipError_t launch_combine_backward(const void* dout, const void* y, const int32_t* pos,
+                                   const float* w, void* dy, float* dw, int T, int k, int H,
+                                   int act, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int cpr = H / 8;
+  const u32x4* g = static_cast<const u32x4*>(dout);
+  const u32x4* yv = static_cast<const u32x4*>(y);
+  u32x4* dyv = static_cast<u32x4*>(dy);
+  return act == 1 ? launch_cb_k<1>(g, yv, pos, w, dyv, dw, T, k, cpr, s)
+                  : launch_cb_k<2>(g, yv, pos, w, dyv, dw, T, k, cpr, s);
+}
+
+hipError_t launch_dispatch_backward(const void* dsend, const int32_t* pos, void* dx, int T, int k,
+                                    int H, int act, bool out_f32, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int cpr = H / 8;
+  const u32x4* d = static_cast<const u32x4*>(dsend);
+  if (act == 1)
+    return out_f32 ? launch_db_k<1, true>(d, pos, dx, T, k, cpr, s)
+                   : launch_db_k<1, false>(d, pos, dx, T, k, cpr, s);
+  return out_f32 ? launch_db_k<2, true>(d, pos, dx, T, k, cpr, s)
+                 : launch_db_k<2, false>(d, pos, dx, T, k, cpr, s);
+}
+
+}  // namespace moe

@@ -52,4 +52,10 @@ hipError_t launch_standin(const void* send, const int32_t* src, const int32_t* i
 hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, void* out, int T, int k,
                           int H, int act, bool out_f32, hipStream_t s);
 
+hipError_t launch_combine_backward(const void* dout, const void* y, const int32_t* pos,
+                                   const float* w, void* dy, float* dw, int T, int k, int H,
+                                   int act, hipStream_t s);
+hipError_t launch_dispatch_backward(const void* dsend, const int32_t* pos, void* dx, int T, int k,
+                                    int H, int act, bool out_f32, hipStream_t s);
+
 }  // namespace moe

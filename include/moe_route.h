@@ -234,6 +234,38 @@ moe_status moe_expert_standin(const moe_problem* p, const void* send, const int3
 moe_status moe_combine(const moe_problem* p, const void* y, const int32_t* pos, const float* w,
                        void* out, void* stream);
 
+/* Backward of the combine. With dout [T, H] the gradient of out:
+ *   dy[pos[t*k + j]] = round16(fp32(w[t, j] * dout[t]))   (one rounding
+ *                      of the fp32 product to the activation format)
+ *   dw[t, j]         = <y[pos[t*k + j]], dout[t]>, summed in fp32
+ * Derived from the forward definition of moe_combine; [CORR] section "Why
+ * communication is the target" (the combine also runs in the backward
+ * pass). One kernel reads each dout row once and, per slot, writes the dy
+ * row and reads the y row for the dot product.
+ *   dout 16-bit [T, H] (read)   pos i32 [T*k] (read)
+ *   w    f32 [T, k] (read; may be NULL when dy is NULL)
+ *   y    16-bit [T*k, H] (read; may be NULL when dw is NULL)
+ *   dy   16-bit [T*k, H] (write, or NULL to skip); may alias y, must not
+ *        overlap dout
+ *   dw   f32 [T, k] (write, or NULL to skip)
+ * With T > 0 at least one of dy, dw must be non-NULL (else
+ * MOE_ERR_INVALID_ARG). A slot whose pos is out of range
+ * writes no dy row and a dw of 0.                                          */
+moe_status moe_combine_backward(const moe_problem* p, const void* dout, const void* y,
+                                const int32_t* pos, const float* w, void* dy, float* dw,
+                                void* stream);
+
+/* Backward of the dispatch: dx[t] = sum over j = 0..k-1 (ascending) of
+ * dsend[pos[t*k + j]], accumulated in fp32, written in the activation format
+ * (round to nearest-even) or as fp32 with MOE_FLAG_OUT_F32. Derived from the
+ * forward definition of moe_dispatch; [CORR] section "Why communication is
+ * the target".
+ *   dsend 16-bit [T*k, H] (read)   pos i32 [T*k] (read)
+ *   dx    [T, H] in the activation format or fp32 (write); must not overlap
+ *         dsend. A slot whose pos is out of range adds nothing.           */
+moe_status moe_dispatch_backward(const moe_problem* p, const void* dsend, const int32_t* pos,
+                                 void* dx, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

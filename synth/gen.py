@@ -18,7 +18,10 @@ Recipe (seed s, workload w):
         p[perm[i]] proportional to (i+1)^-1, bias 0.5 * log p;
   * activations: standard normal float32 drawn in chunks of 4096 rows, rounded
     to nearest-even into fp16 (numpy) or bf16 (torch's CPU conversion), and
-    returned as uint16 bit patterns [T, H].
+    returned as uint16 bit patterns [T, H];
+  * upstream gradients for the backward (make_grad): the same row recipe from
+    a fourth generator of the seed's SeedSequence (children 3 + stream), so
+    they are independent of the logits and activations.
 """
 from __future__ import annotations
 
@@ -63,19 +66,29 @@ def _to_bf16_bits(f32: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def make_x(w: Workload, seed: int = 0) -> np.ndarray:
-    _, _, g_x = _streams(seed)
-    out = np.empty((w.T, w.H), dtype=np.uint16)
-    for r0 in range(0, w.T, X_CHUNK_ROWS):
-        rows = min(X_CHUNK_ROWS, w.T - r0)
-        f = g_x.standard_normal((rows, w.H), dtype=np.float32)
-        if w.act_dtype == F16:
+def _rows16(g: np.random.Generator, n: int, H: int, act_dtype: int) -> np.ndarray:
+    out = np.empty((n, H), dtype=np.uint16)
+    for r0 in range(0, n, X_CHUNK_ROWS):
+        rows = min(X_CHUNK_ROWS, n - r0)
+        f = g.standard_normal((rows, H), dtype=np.float32)
+        if act_dtype == F16:
             out[r0:r0 + rows] = f.astype(np.float16).view(np.uint16)
-        elif w.act_dtype == BF16:
+        elif act_dtype == BF16:
             out[r0:r0 + rows] = _to_bf16_bits(f)
         else:
             raise ValueError("act_dtype")
     return out
+
+
+def make_x(w: Workload, seed: int = 0) -> np.ndarray:
+    _, _, g_x = _streams(seed)
+    return _rows16(g_x, w.T, w.H, w.act_dtype)
+
+
+def make_grad(w: Workload, seed: int, rows: int, stream: int = 0) -> np.ndarray:
+    """Seeded upstream-gradient rows [rows, H] as uint16 bit patterns."""
+    g = np.random.default_rng(np.random.SeedSequence(seed).spawn(4 + stream)[3 + stream])
+    return _rows16(g, rows, w.H, w.act_dtype)
 
 
 def digest(a: np.ndarray) -> str:

@@ -40,3 +40,12 @@ def test_decode_replica_table():
     assert ((rep[:, 1] >= 0) == (np.arange(256) % 8 == 0)).all()
     assert (rep[::8, 1] == (np.arange(0, 256, 8) // 32 + 4) % 8).all()
     assert synth.replica_table(synth.TRAIN_TOP2) is None
+
+
+def test_grad_rows_seeded_and_independent():
+    w = synth.scaled(synth.TRAIN_TOP6, T=100, H=64)
+    a, b = synth.make_grad(w, 3, 50), synth.make_grad(w, 3, 50)
+    assert a.shape == (50, 64) and a.dtype == np.uint16 and np.array_equal(a, b)
+    assert not np.array_equal(a, synth.make_grad(w, 3, 50, stream=1))
+    assert not np.array_equal(a, synth.make_x(w, 3)[:50])
+    assert not np.array_equal(a, synth.make_grad(w, 4, 50))
