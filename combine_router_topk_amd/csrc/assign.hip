@@ -1,4 +1,4 @@
-// Greedy replica assignment ("activated-expert minimisation").
+// Greedy replica assignment: the kernel that keeps the activated experts per GPU small.
 //
 // "METRO AllGather vs AllToAll for MoE decode", section "METRO AllGather vs
 // AllToAll changes the routing information" (each active expert is served by
