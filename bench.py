@@ -10,9 +10,9 @@ are flushed (a 1 GiB fill) before the dispatch and before the combine, outside
 their event brackets, so both read from HBM.
 
 After the headline loop, and outside it, the same batch also times the
-single-send variant (layout, one-row-per-rank dispatch, receiver fan-out) and
-the backward of the dispatch and the combine; each is reported in its own
-object of the JSON line.
+single-send variant (layout, one-row-per-rank dispatch, receiver fan-out), the
+backward of the dispatch and the combine, and the routing statistics; each is
+reported in its own object of the JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line.
@@ -48,6 +48,8 @@ def parse():
                     help="timed passes of the single-send variant after the headline loop (0 = skip)")
     ap.add_argument("--backward-steps", type=int, default=20,
                     help="timed passes of the dispatch/combine backward after the headline loop (0 = skip)")
+    ap.add_argument("--stats-steps", type=int, default=20,
+                    help="timed calls of the routing statistics after the headline loop (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 30,
                     help="tokens in the oracle's CPU-baseline sample (0 = skip; default all)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -195,6 +197,35 @@ def backward_leg(B, w, b, flush, steps, ev, np, torch, synth, seed):
             "combine_backward_bytes": cb_bytes, "dispatch_backward_bytes": db_bytes}
 
 
+def stats_leg(P, w, b, steps, ev, np, torch):
+    """Routing statistics of the batch (send-counts matrix, co-selection
+    histogram, max/mean, Gini, Dirichlet alpha, locality), timed over
+    `steps` calls; plus the share of the tokens' expert pairs held by the
+    most frequent 0.8% of pairs, read from the co-selection histogram."""
+    st = P.allocate_stats(b)
+    marks = []
+    for i in range(steps + 2):
+        a, c = ev(), ev()
+        a.record()
+        P.routing_stats(b, st)
+        c.record()
+        if i >= 2:
+            marks.append((a, c))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(c) for a, c in marks]))
+    vals = st.stats.cpu().numpy()
+    C = st.coselect.cpu().numpy().astype(np.int64)
+    E = w.E
+    iu = np.triu_indices(E, 1)
+    pairs = np.sort(C[iu])[::-1]
+    top = int(np.ceil(0.008 * pairs.shape[0]))
+    cover = float(pairs[:top].sum()) / max(1, int(pairs.sum()))
+    f = lambda v: None if not np.isfinite(v) else round(float(v), 6)
+    return {"steps": steps, "ms": round(ms, 4), "max_over_mean": f(vals[0]), "gini": f(vals[1]),
+            "dirichlet_alpha": f(vals[2]), "locality": f(vals[3]),
+            "top_0.8pct_pairs_share": round(cover, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -321,6 +352,8 @@ def main():
     if args.backward_steps > 0:
         res["backward"] = backward_leg(B, w, b, flush, args.backward_steps, ev, np, torch, synth,
                                        args.seed)
+    if args.stats_steps > 0:
+        res["routing_stats"] = stats_leg(P, w, b, args.stats_steps, ev, np, torch)
     if args.cpu_tokens > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_tokens, args.cpu_seconds)
     print(json.dumps(res), flush=True)

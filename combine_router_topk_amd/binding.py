@@ -25,7 +25,8 @@ MOE_FLAG_OUT_F32 = 1 << 1
 EXPORTED = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
             "moe_route", "moe_assign_replicas", "moe_layout", "moe_layout_single_send",
             "moe_single_send_dispatch", "moe_single_send_expand", "moe_dispatch",
-            "moe_expert_standin", "moe_combine", "moe_combine_backward", "moe_dispatch_backward")
+            "moe_expert_standin", "moe_combine", "moe_combine_backward", "moe_dispatch_backward",
+            "moe_routing_stats")
 
 _TORCH_ACT = {MOE_F16: torch.float16, MOE_BF16: torch.bfloat16}
 
@@ -69,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "moe_combine": (i32, [P, vp, vp, vp, vp, vp]),
         "moe_combine_backward": (i32, [P, vp, vp, vp, vp, vp, vp, vp]),
         "moe_dispatch_backward": (i32, [P, vp, vp, vp, vp]),
+        "moe_routing_stats": (i32, [P, vp, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -254,3 +256,15 @@ def moe_dispatch_backward(p: Problem, dsend, pos, dx, stream=None) -> None:
                                       _ptr(pos, torch.int32, n, "pos"),
                                       _ptr(dx, out_dt, p.T * p.H, "dx"), _stream(stream)),
            "moe_dispatch_backward")
+
+
+def moe_routing_stats(p: Problem, idx, counts, rank_of, send_counts, coselect, stats,
+                      stream=None) -> None:
+    """coselect may be None; stats is a float64 tensor of 4."""
+    _check(_lib.moe_routing_stats(ctypes.byref(p), _ptr(idx, torch.int32, p.T * p.k, "idx"),
+                                  _ptr(counts, torch.int32, p.E, "counts"),
+                                  _ptr(rank_of, torch.int32, p.E, "rank_of"),
+                                  _ptr(send_counts, torch.int32, p.R * p.R, "send_counts"),
+                                  _ptr(coselect, torch.int32, p.E * p.E, "coselect"),
+                                  _ptr(stats, torch.float64, 4, "stats"), _stream(stream)),
+           "moe_routing_stats")

@@ -310,4 +310,22 @@ moe_status moe_dispatch_backward(const moe_problem* p, const void* dsend, const 
                     fn);
 }
 
+moe_status moe_routing_stats(const moe_problem* p, const int32_t* idx, const int32_t* counts,
+                             const int32_t* rank_of, int32_t* send_counts, int32_t* coselect,
+                             double* stats, void* stream) {
+  const char* fn = "moe_routing_stats";
+  CHECK(check_problem(p, fn));
+  CHECK(need(counts, 4, fn, "counts"));
+  CHECK(need(rank_of, 4, fn, "rank_of"));
+  CHECK(need(send_counts, 4, fn, "send_counts"));
+  CHECK(need(stats, 8, fn, "stats"));
+  if (coselect != nullptr) CHECK(need(coselect, 4, fn, "coselect"));
+  if (p->T > 0) CHECK(need(idx, 4, fn, "idx"));
+  clear_stale_error();
+  return hip_status(moe::launch_routing_stats(idx, rank_of, counts, p->T, p->E, p->k, p->R,
+                                              send_counts, coselect, stats,
+                                              static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

@@ -58,4 +58,8 @@ hipError_t launch_combine_backward(const void* dout, const void* y, const int32_
 hipError_t launch_dispatch_backward(const void* dsend, const int32_t* pos, void* dx, int T, int k,
                                     int H, int act, bool out_f32, hipStream_t s);
 
+hipError_t launch_routing_stats(const int32_t* idx, const int32_t* rank_of, const int32_t* counts,
+                                int T, int E, int k, int R, int32_t* S, int32_t* C, double* stats,
+                                hipStream_t s);
+
 }  // namespace moe

@@ -129,3 +129,24 @@ def single_send_expand(b: Buffers, ss: SingleSend, stream=None) -> None:
     """Fills b.send from the single-send rows (what dispatch writes)."""
     B.moe_single_send_expand(b.p, ss.send_ss, ss.ss_rank_offsets, ss.ss_token, ss.ss_row, b.pos,
                              b.send, stream)
+
+
+@dataclass
+class Stats:
+    """Routing-statistics outputs: send_counts [R, R], coselect [E, E] (or
+    None), stats [4] = max/mean, Gini, Dirichlet alpha, locality."""
+    send_counts: torch.Tensor
+    coselect: torch.Tensor | None
+    stats: torch.Tensor
+
+
+def allocate_stats(b: Buffers, coselect: bool = True) -> Stats:
+    p, dev = b.p, b.idx.device
+    return Stats(send_counts=torch.empty(p.R, p.R, dtype=torch.int32, device=dev),
+                 coselect=torch.empty(p.E, p.E, dtype=torch.int32, device=dev) if coselect else None,
+                 stats=torch.empty(4, dtype=torch.float64, device=dev))
+
+
+def routing_stats(b: Buffers, st: Stats, stream=None) -> None:
+    B.moe_routing_stats(b.p, b.idx, b.counts, b.rank_of, st.send_counts, st.coselect, st.stats,
+                        stream)

@@ -9,6 +9,8 @@
  *   [METRO]  "METRO AllGather vs AllToAll for MoE decode" (fanout.sh).
  *   [CORR]   News summary of "correlated expert placement and token
  *            shuffling" for MoE pretraining (ainewsletter.today).
+ *   [DODOCO] "Diagnosing Overhead in Dispatch Operations: Cross-architecture
+ *            Observatory" (gist.science).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -265,6 +267,32 @@ moe_status moe_combine_backward(const moe_problem* p, const void* dout, const vo
  *         dsend. A slot whose pos is out of range adds nothing.           */
 moe_status moe_dispatch_backward(const moe_problem* p, const void* dsend, const int32_t* pos,
                                  void* dx, void* stream);
+
+/* Routing statistics of one batch. [DODOCO] section "Methodology" (three
+ * scalar summaries of the send-counts matrix: per-expert max/mean, Gini of
+ * the per-rank load, a fitted symmetric Dirichlet alpha); [CORR] sections
+ * "Correlations in router choices" (experts chosen together) and "Two
+ * locality techniques" (share of assignments served on the token's own GPU).
+ * Token t comes from virtual rank floor(t R / T).
+ *   idx         i32 [T, k] (read)   counts i32 [E] (read, from moe_route)
+ *   rank_of     i32 [E] (read, from moe_layout)
+ *   send_counts i32 [R, R] (write): [s][d] = (token, slot) pairs from
+ *               source rank s whose expert sits on rank d
+ *   coselect    i32 [E, E] (write, or NULL to skip): [a][b] for a < b = the
+ *               tokens that chose both a and b; 0 elsewhere
+ *   stats       f64 [4] (write): with N = T k and L[d] = sum_s S[s][d],
+ *               [0] max_e counts[e] / (N / E)
+ *               [1] Gini of L: sum_i sum_j |L_i - L_j| / (2 R N)
+ *               [2] symmetric Dirichlet alpha fitted by moments to the
+ *                   shares L / N: ((R - 1) / (R D) - 1) / R with
+ *                   D = sum_i (L_i / N - 1/R)^2; +inf when D = 0
+ *               [3] locality: sum_r S[r][r] / N
+ *               all four NaN when T = 0.
+ * Every count is exact (integer adds); the ratios are a few fp64 operations
+ * on exact integers.                                                        */
+moe_status moe_routing_stats(const moe_problem* p, const int32_t* idx, const int32_t* counts,
+                             const int32_t* rank_of, int32_t* send_counts, int32_t* coselect,
+                             double* stats, void* stream);
 
 #ifdef __cplusplus
 }
