@@ -27,5 +27,7 @@ from .pipeline import route_and_layout, rows_for  # noqa: F401
 from .single_send import (single_send_dispatch, single_send_expand,  # noqa: F401
                           single_send_layout)
 from .backward import combine_backward_dw, combine_backward_dy, dispatch_backward  # noqa: F401
+from .eplb import (optimal_max_activated, replica_share_index,  # noqa: F401
+                   split_tokens_per_gpu, token_balanced_split)
 from .stats import (coselection, dirichlet_alpha, gini, routing_stats,  # noqa: F401
                     send_counts, source_ranks, top_pair_coverage)

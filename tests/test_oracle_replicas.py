@@ -1,7 +1,6 @@
 """Pins for the oracle's METRO greedy replica assignment: the page's toy
 example, the decode-table closed form derived by hand, a hand-worked instance,
 invariants, and an exhaustive optimum on tiny instances (no GPU)."""
-import itertools
 import math
 
 import numpy as np
@@ -86,26 +85,16 @@ def test_no_replicas_is_per_rank_active_count():
     assert all(assign[e] == (e // per if counts[e] else -1) for e in range(E))
 
 
-def exhaustive_optimum(counts, R, rep):
-    act_e = [e for e in range(len(counts)) if counts[e] > 0]
-    cands = [[g for g in rep[e] if g >= 0] for e in act_e]
-    best = None
-    for choice in itertools.product(*cands):
-        m = max(np.bincount(np.array(choice, dtype=np.int64), minlength=R)) if choice else 0
-        best = m if best is None else min(best, m)
-    return best or 0
-
-
 @pytest.mark.parametrize("seed", range(12))
 def test_greedy_against_exhaustive_optimum(seed):
     rng = np.random.default_rng(1000 + seed)
     E, R = 10, 4
     rep, counts = random_instance(rng, E, R, 2, 0.8)
     _, act = oracle.greedy_assign(counts, R, rep)
-    opt = exhaustive_optimum(counts, R, rep)
+    opt = oracle.optimal_max_activated(counts, R, rep)
     assert act.max() >= opt
     # single-copy experts leave no choice: greedy equals the optimum then
     single = rep.copy()
     single[:, 1:] = -1
     _, act1 = oracle.greedy_assign(counts, R, single)
-    assert act1.max() == exhaustive_optimum(counts, R, single)
+    assert act1.max() == oracle.optimal_max_activated(counts, R, single)
