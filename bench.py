@@ -11,8 +11,9 @@ their event brackets, so both read from HBM.
 
 After the headline loop, and outside it, the same batch also times the
 single-send variant (layout, one-row-per-rank dispatch, receiver fan-out), the
-backward of the dispatch and the combine, and the routing statistics; each is
-reported in its own object of the JSON line.
+backward of the dispatch and the combine, and the routing statistics, and
+the replicated decode workload compares the greedy replica assignment with
+token-balanced routing; each is reported in its own object of the JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line.
@@ -50,6 +51,8 @@ def parse():
                     help="timed passes of the dispatch/combine backward after the headline loop (0 = skip)")
     ap.add_argument("--stats-steps", type=int, default=20,
                     help="timed calls of the routing statistics after the headline loop (0 = skip)")
+    ap.add_argument("--eplb-steps", type=int, default=20,
+                    help="timed token-balanced splits on the replicated decode workload (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 30,
                     help="tokens in the oracle's CPU-baseline sample (0 = skip; default all)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -226,6 +229,42 @@ def stats_leg(P, w, b, steps, ev, np, torch):
             "top_0.8pct_pairs_share": round(cover, 4)}
 
 
+def eplb_leg(P, B, synth, np, torch, dev, steps, ev, seed):
+    """The greedy replica assignment against token-balanced (EPLB-style)
+    routing on the replicated decode workload (the one workload with
+    replicas): maximum activated experts and maximum pairs per GPU under
+    each, and the time of the token-balanced split."""
+    w = synth.DECODE
+    logits, x = synth.make_logits(w, seed), synth.make_x(w, seed)
+    rep = synth.replica_table(w)
+    tdt = torch.float16 if w.act_dtype == synth.F16 else torch.bfloat16
+    p = B.make_problem(w.T, w.E, w.k, w.H, w.R, w.act_dtype)
+    b = P.allocate(p, torch.from_numpy(logits), torch.from_numpy(x.view(np.int16)).view(tdt),
+                   torch.from_numpy(rep), device=dev)
+    P.route(b)
+    P.assign(b)
+    P.layout(b)
+    sp = P.allocate_split(b)
+    marks = []
+    for i in range(steps + 2):
+        a, c = ev(), ev()
+        a.record()
+        P.token_balanced_split(b, sp)
+        c.record()
+        if i >= 2:
+            marks.append((a, c))
+    torch.cuda.synchronize()
+    g_act = int(b.active.max().item())
+    e_act = int(sp.active.max().item())
+    g_tok = int((b.rank_offsets[1:] - b.rank_offsets[:-1]).max().item())
+    e_tok = int(sp.tokens.max().item())
+    return {"workload": w.name, "steps": steps,
+            "ms": round(float(np.mean([a.elapsed_time(c) for a, c in marks])), 4),
+            "max_activated": {"greedy": g_act, "token_balanced": e_act},
+            "greedy_below_token_balanced": round(1 - g_act / e_act, 4) if e_act else None,
+            "max_pairs_per_gpu": {"greedy": g_tok, "token_balanced": e_tok}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -354,6 +393,8 @@ def main():
                                        args.seed)
     if args.stats_steps > 0:
         res["routing_stats"] = stats_leg(P, w, b, args.stats_steps, ev, np, torch)
+    if args.eplb_steps > 0:
+        res["eplb"] = eplb_leg(P, B, synth, np, torch, dev, args.eplb_steps, ev, args.seed)
     if args.cpu_tokens > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_tokens, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -13,6 +13,7 @@ from .binding import (MOE_BF16, MOE_F16, MOE_FLAG_GREEDY_ID_ORDER, MOE_FLAG_OUT_
                       moe_combine_backward, moe_dispatch_backward,
                       moe_dispatch, moe_expert_standin, moe_last_error, moe_layout,
                       moe_layout_single_send, moe_route, moe_routing_stats, moe_single_send_dispatch,
-                      moe_single_send_expand, moe_status_string, moe_version,
+                      moe_single_send_expand, moe_status_string, moe_token_balanced_split,
+                      moe_version,
                       moe_workspace_bytes)
 from . import path  # noqa: F401

@@ -26,7 +26,7 @@ EXPORTED = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace
             "moe_route", "moe_assign_replicas", "moe_layout", "moe_layout_single_send",
             "moe_single_send_dispatch", "moe_single_send_expand", "moe_dispatch",
             "moe_expert_standin", "moe_combine", "moe_combine_backward", "moe_dispatch_backward",
-            "moe_routing_stats")
+            "moe_routing_stats", "moe_token_balanced_split")
 
 _TORCH_ACT = {MOE_F16: torch.float16, MOE_BF16: torch.bfloat16}
 
@@ -71,6 +71,7 @@ def _load() -> ctypes.CDLL:
         "moe_combine_backward": (i32, [P, vp, vp, vp, vp, vp, vp, vp]),
         "moe_dispatch_backward": (i32, [P, vp, vp, vp, vp]),
         "moe_routing_stats": (i32, [P, vp, vp, vp, vp, vp, vp, vp]),
+        "moe_token_balanced_split": (i32, [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -268,3 +269,14 @@ def moe_routing_stats(p: Problem, idx, counts, rank_of, send_counts, coselect, s
                                   _ptr(coselect, torch.int32, p.E * p.E, "coselect"),
                                   _ptr(stats, torch.float64, 4, "stats"), _stream(stream)),
            "moe_routing_stats")
+
+
+def moe_token_balanced_split(p: Problem, idx, counts, pos, expert_offsets, rep, maxrep: int,
+                             gpu_of_pair, active, tokens, stream=None) -> None:
+    n = p.T * p.k
+    _check(_lib.moe_token_balanced_split(
+        ctypes.byref(p), _ptr(idx, torch.int32, n, "idx"), _ptr(counts, torch.int32, p.E, "counts"),
+        _ptr(pos, torch.int32, n, "pos"), _ptr(expert_offsets, torch.int32, p.E, "expert_offsets"),
+        _ptr(rep, torch.int32, p.E * maxrep if rep is not None else 0, "rep"), maxrep,
+        _ptr(gpu_of_pair, torch.int32, n, "gpu_of_pair"), _ptr(active, torch.int32, p.R, "active"),
+        _ptr(tokens, torch.int32, p.R, "tokens"), _stream(stream)), "moe_token_balanced_split")

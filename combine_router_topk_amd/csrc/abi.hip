@@ -328,4 +328,29 @@ moe_status moe_routing_stats(const moe_problem* p, const int32_t* idx, const int
                     fn);
 }
 
+moe_status moe_token_balanced_split(const moe_problem* p, const int32_t* idx,
+                                    const int32_t* counts, const int32_t* pos,
+                                    const int32_t* expert_offsets, const int32_t* rep,
+                                    int32_t maxrep, int32_t* gpu_of_pair, int32_t* active,
+                                    int32_t* tokens, void* stream) {
+  const char* fn = "moe_token_balanced_split";
+  CHECK(check_problem(p, fn));
+  CHECK(check_rep(p, rep, maxrep, fn));
+  CHECK(need(counts, 4, fn, "counts"));
+  CHECK(need(active, 4, fn, "active"));
+  CHECK(need(tokens, 4, fn, "tokens"));
+  if (p->T > 0 && gpu_of_pair != nullptr) {
+    CHECK(need(idx, 4, fn, "idx"));
+    CHECK(need(pos, 4, fn, "pos"));
+    CHECK(need(expert_offsets, 4, fn, "expert_offsets"));
+    CHECK(need(gpu_of_pair, 4, fn, "gpu_of_pair"));
+  }
+  clear_stale_error();
+  return hip_status(moe::launch_token_balanced_split(idx, counts, pos, expert_offsets, rep,
+                                                     rep ? maxrep : 1, p->T, p->E, p->k, p->R,
+                                                     gpu_of_pair, active, tokens,
+                                                     static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

@@ -62,4 +62,10 @@ hipError_t launch_routing_stats(const int32_t* idx, const int32_t* rank_of, cons
                                 int T, int E, int k, int R, int32_t* S, int32_t* C, double* stats,
                                 hipStream_t s);
 
+hipError_t launch_token_balanced_split(const int32_t* idx, const int32_t* counts,
+                                       const int32_t* pos, const int32_t* expert_offsets,
+                                       const int32_t* rep, int maxrep, int T, int E, int k, int R,
+                                       int32_t* gpu_of_pair, int32_t* active, int32_t* tokens,
+                                       hipStream_t s);
+
 }  // namespace moe

@@ -150,3 +150,24 @@ def allocate_stats(b: Buffers, coselect: bool = True) -> Stats:
 def routing_stats(b: Buffers, st: Stats, stream=None) -> None:
     B.moe_routing_stats(b.p, b.idx, b.counts, b.rank_of, st.send_counts, st.coselect, st.stats,
                         stream)
+
+
+@dataclass
+class Split:
+    """Token-balanced (EPLB-style) routing outputs: the GPU of each pair and,
+    per GPU, the activated replicas and the pairs served."""
+    gpu_of_pair: torch.Tensor
+    active: torch.Tensor
+    tokens: torch.Tensor
+
+
+def allocate_split(b: Buffers) -> Split:
+    p, dev = b.p, b.idx.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    return Split(gpu_of_pair=torch.empty(p.T * p.k, **i32), active=torch.empty(p.R, **i32),
+                 tokens=torch.empty(p.R, **i32))
+
+
+def token_balanced_split(b: Buffers, sp: Split, stream=None) -> None:
+    B.moe_token_balanced_split(b.p, b.idx, b.counts, b.pos, b.expert_offsets, b.rep, b.maxrep,
+                               sp.gpu_of_pair, sp.active, sp.tokens, stream)

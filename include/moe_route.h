@@ -294,6 +294,31 @@ moe_status moe_routing_stats(const moe_problem* p, const int32_t* idx, const int
                              const int32_t* rank_of, int32_t* send_counts, int32_t* coselect,
                              double* stats, void* stream);
 
+/* Token-balanced (EPLB-style) replica routing, the baseline the greedy of
+ * moe_assign_replicas is compared against. [METRO] section "Add the
+ * expert-weight traffic term" (balancing tokens over an expert's replicas
+ * activates more replicas per GPU than grouping them; the greedy is
+ * reported against EPLB's token routing).
+ * The n pairs routed to expert e, in the order of e's send segment (token
+ * order), are cut into contiguous shares over e's valid replicas (entries
+ * of rep[e] in [0, R), in table order): with m of them, replica j takes
+ * n / m pairs, plus one when j < n mod m. rep = NULL: one copy per expert,
+ * on rank e / (E / R).
+ *   idx            i32 [T, k] (read)   counts i32 [E] (read, from moe_route)
+ *   pos            i32 [T*k] (read)    expert_offsets i32 [E] (read), both
+ *                  from moe_layout (any rank order: only the place of a
+ *                  pair inside its expert's segment is used)
+ *   rep, maxrep    as for moe_assign_replicas
+ *   gpu_of_pair    i32 [T*k] (write, or NULL to skip): the GPU serving each
+ *                  pair; -1 for an expert without a valid replica
+ *   active         i32 [R] (write): replicas with a non-empty share per GPU
+ *   tokens         i32 [R] (write): pairs served per GPU                    */
+moe_status moe_token_balanced_split(const moe_problem* p, const int32_t* idx,
+                                    const int32_t* counts, const int32_t* pos,
+                                    const int32_t* expert_offsets, const int32_t* rep,
+                                    int32_t maxrep, int32_t* gpu_of_pair, int32_t* active,
+                                    int32_t* tokens, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
