@@ -119,3 +119,33 @@ def test_optimum_refuses_large_searches():
     rep = synth.replica_table(synth.DECODE)
     with pytest.raises(ValueError):
         ep.optimal_max_activated(np.ones(256, np.int32), 8, rep)
+
+
+def test_greedy_gap_report():
+    """The greedy against the optimum and against token balance on 300 seeded
+    small instances (12 experts, 4 GPUs, one or two copies each): printed as
+    the comparison the page reports; the asserts are the invariants."""
+    n = n_opt = 0
+    gaps, below_bal = [], []
+    for seed in range(300):
+        rng = np.random.default_rng(5000 + seed)
+        E, R = 12, 4
+        rep = np.full((E, 2), -1, np.int32)
+        for e in range(E):
+            m = int(rng.integers(1, 3))
+            rep[e, :m] = rng.choice(R, size=m, replace=False)
+        counts = ((rng.random(E) < 0.8) * rng.integers(1, 5, E)).astype(np.int32)
+        if counts.sum() == 0:
+            continue
+        opt = ep.optimal_max_activated(counts, R, rep)
+        _, act = oracle.greedy_assign(counts, R, rep)
+        bal = oracle.token_balanced_activations(counts, R, rep)
+        assert act.max() >= opt and bal.max() >= opt
+        n += 1
+        n_opt += int(act.max() == opt)
+        gaps.append(act.max() / opt - 1)
+        below_bal.append(1 - act.max() / bal.max())
+    print(f"greedy optimal on {n_opt}/{n}; gap to optimum mean {np.mean(gaps):.3f} "
+          f"max {max(gaps):.3f}; below token balance mean {np.mean(below_bal):.3f} "
+          f"max {max(below_bal):.3f}")
+    assert n > 250
