@@ -52,7 +52,7 @@ __device__ __forceinline__ void grad_team(int tpt, int& t, int& lt, int& stride)
 // waves in order). Slots whose pos is out of range write no dy row and a dw
 // of 0. dy may alias y: every chunk of y is read before the same lane
 // writes that chunk of dy.
-template <int ACT, int KMAX, bool ONE>
+template <int ACT, int KMAX, bool ONE, int U>
 __global__ __launch_bounds__(kGradThreads) void combine_backward_kernel(
     const u32x4* __restrict__ dout, const u32x4* y, const int32_t* __restrict__ pos,
     const float* __restrict__ w, u32x4* dy, float* __restrict__ dw, int T, int k, int cpr,
@@ -83,35 +83,50 @@ __global__ __launch_bounds__(kGradThreads) void combine_backward_kernel(
     }
   }
   if (live) {
+    // U chunk positions per step: every load of the step (U dout chunks and,
+    // for dw, U * k y chunks) is issued before any math or store
     const u32x4* g_row = dout + (size_t)t * cpr;
-    for (int c = lt; c < cpr; c += stride) {
-      float g[8];
-      unpack8<ACT>(as_uint4(__builtin_nontemporal_load(g_row + c)), g);
-      if (do_dw) {
-        u32x4 v[KMAX];
+    for (int c0 = lt; c0 < cpr; c0 += stride * U) {
+      u32x4 gv[U];
+      u32x4 v[U][KMAX];
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j)
-          if (j < k && ok[j]) v[j] = __builtin_nontemporal_load(y + row[j] + c);
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * stride;
+        if (c < cpr) gv[u] = __builtin_nontemporal_load(g_row + c);
+        if (do_dw) {
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-          if (j < k && ok[j]) {
-            float f[8];
-            unpack8<ACT>(as_uint4(v[j]), f);
-            float s = part[j];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) s = fmaf(f[i], g[i], s);
-            part[j] = s;
-          }
+          for (int j = 0; j < KMAX; ++j)
+            if (j < k && ok[j] && c < cpr) v[u][j] = __builtin_nontemporal_load(y + row[j] + c);
         }
       }
-      if (do_dy) {
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-          if (j < k && ok[j]) {
-            float p[8];
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * stride;
+        if (c >= cpr) break;
+        float g[8];
+        unpack8<ACT>(as_uint4(gv[u]), g);
+        if (do_dw) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) p[i] = keep_f32(wt[j] * g[i]);  // fp32 product, then one rounding
-            __builtin_nontemporal_store(as_vec(pack8<ACT>(p)), dy + row[j] + c);
+          for (int j = 0; j < KMAX; ++j) {
+            if (j < k && ok[j]) {
+              float f[8];
+              unpack8<ACT>(as_uint4(v[u][j]), f);
+              float s = part[j];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) s = fmaf(f[i], g[i], s);
+              part[j] = s;
+            }
+          }
+        }
+        if (do_dy) {
+#pragma unroll
+          for (int j = 0; j < KMAX; ++j) {
+            if (j < k && ok[j]) {
+              float p[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) p[i] = keep_f32(wt[j] * g[i]);  // fp32 product, then one rounding
+              __builtin_nontemporal_store(as_vec(pack8<ACT>(p)), dy + row[j] + c);
+            }
           }
         }
       }
@@ -219,13 +234,20 @@ int grad_threads_per_row(int cpr) {
 template <int ACT, int KMAX>
 hipError_t launch_cb(const u32x4* dout, const u32x4* y, const int32_t* pos, const float* w,
                      u32x4* dy, float* dw, int T, int k, int cpr, hipStream_t s) {
+  if constexpr (KMAX <= 8) {
+    if (cpr > kGradThreads) {  // long rows: two chunk positions per step
+      combine_backward_kernel<ACT, KMAX, true, 2><<<T, kGradThreads, 0, s>>>(
+          dout, y, pos, w, dy, dw, T, k, cpr, kGradThreads);
+      return hipGetLastError();
+    }
+  }
   if (cpr >= kGradOneRowChunks) {
-    combine_backward_kernel<ACT, KMAX, true><<<T, kGradThreads, 0, s>>>(dout, y, pos, w, dy, dw, T,
-                                                                       k, cpr, kGradThreads);
+    combine_backward_kernel<ACT, KMAX, true, 1><<<T, kGradThreads, 0, s>>>(dout, y, pos, w, dy, dw,
+                                                                          T, k, cpr, kGradThreads);
   } else {
     const int tpt = grad_threads_per_row(cpr);
     const int per_blk = kGradThreads / tpt;
-    combine_backward_kernel<ACT, KMAX, false><<<(T + per_blk - 1) / per_blk, kGradThreads, 0, s>>>(
+    combine_backward_kernel<ACT, KMAX, false, 1><<<(T + per_blk - 1) / per_blk, kGradThreads, 0, s>>>(
         dout, y, pos, w, dy, dw, T, k, cpr, tpt);
   }
   return hipGetLastError();

@@ -5,7 +5,8 @@
 // one demand count per expert is formed from all of them.
 //
 // Kernel 1 (route_topk): a group of L lanes owns one token's row of E logits
-// (V = E/L values per lane, coalesced loads). Each of the k rounds takes the
+// (V = E/L values per lane, coalesced loads; the next token's logits are in
+// flight while the current one is processed). Each of the k rounds takes the
 // group maximum of order-preserving 32-bit keys with DPP butterflies (and
 // readlane across 16-lane rows) and then the lowest expert id holding that
 // key with ballots, so ties resolve to the lower id without 64-bit
@@ -44,14 +45,33 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   const int t_begin = blockIdx.x * tpb;
   const int t_end = min(T, t_begin + tpb);
 
-  for (int t0 = t_begin + wave * TPW; t0 < t_end; t0 += nwaves * TPW) {
+  // the next step's logits are loaded before the current token is processed
+  const int tstep = nwaves * TPW;
+  float nxt[V];
+  {
+    const int t = t_begin + wave * TPW + grp;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = sl + v * L;
+      nxt[v] = (t < t_end && e < E) ? logits[(size_t)t * E + e] : 0.0f;
+    }
+  }
+  for (int t0 = t_begin + wave * TPW; t0 < t_end; t0 += tstep) {
     const int t = t0 + grp;
     const bool valid = t < t_end;
     uint32_t key[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const int e = sl + v * L;
-      key[v] = (valid && e < E) ? logit_key(logits[(size_t)t * E + e]) : 0u;
+      key[v] = (valid && e < E) ? logit_key(nxt[v]) : 0u;
+    }
+    {
+      const int tn = t + tstep;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int e = sl + v * L;
+        nxt[v] = (tn < t_end && e < E) ? logits[(size_t)tn * E + e] : 0.0f;
+      }
     }
     int my_e = 0;
     uint32_t my_key = 0u, top_key = 0u;

@@ -125,15 +125,29 @@ __global__ __launch_bounds__(kFinalThreads) void stats_finalize_kernel(
     double* __restrict__ stats) {
   __shared__ int64_t s_load[kMaxR];
   __shared__ int64_t s_red[kFinalThreads / kWave];
+  __shared__ int s_part[kFinalThreads];
   const int tid = threadIdx.x;  // E, R <= 1024 == blockDim.x
   const int64_t N = (int64_t)T * k;
   int64_t my_max = 0, diag = 0, load = 0;
   if (tid < E) my_max = counts[tid];
+  // column sums of S: G = 1024 / R groups of rows, each thread summing one
+  // column over its group's rows with several loads in flight, then the
+  // group partials added in order
+  const int G = R >= kFinalThreads ? 1 : kFinalThreads / R;
+  if (tid < G * R) {
+    const int c = tid % R, g = tid / R;
+    int part = 0;
+#pragma unroll 8
+    for (int s = g; s < R; s += G) part += S[(size_t)s * R + c];
+    s_part[tid] = part;
+  }
+  __syncthreads();
   if (tid < R) {
-    for (int s = 0; s < R; ++s) load += S[(size_t)s * R + tid];
+    for (int g = 0; g < G; ++g) load += s_part[g * R + tid];
     s_load[tid] = load;
     diag = S[(size_t)tid * R + tid];
   }
+  __syncthreads();
   // block maximum of the counts
   for (int off = kWave / 2; off > 0; off /= 2) {
     const int64_t o = __shfl_xor(my_max, off);
