@@ -69,6 +69,9 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(
   const int n_rows = SS ? capacity : T * k;
   const u32x4* xr = x + (size_t)t * cpr;
   const int32_t* pr = pos + (size_t)t * k;
+  // SS: bit j set when slot j is the first of the token to carry its row;
+  // formed once, while the first row loads are in flight
+  uint32_t first = 0;
   for (int c0 = lt; c0 < cpr; c0 += stride * U) {
     u32x4 v[U];
 #pragma unroll
@@ -77,13 +80,21 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(
       if (c < cpr) v[u] = __builtin_nontemporal_load(xr + c);
       if constexpr (SERIAL) __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
+    if constexpr (SS) {
+      if (c0 == lt) {
+        for (int j = 0; j < k; ++j) {
+          const int r = pr[j];
+          bool dup = false;
+          for (int jj = 0; jj < j; ++jj) dup |= (pr[jj] == r);
+          first |= dup ? 0u : (1u << j);
+        }
+      }
+    }
     for (int j = 0; j < k; ++j) {
       const int r = pr[j];
       if (static_cast<unsigned>(r) >= static_cast<unsigned>(n_rows)) continue;  // bad pos: skipped
       if constexpr (SS) {
-        bool dup = false;
-        for (int jj = 0; jj < j; ++jj) dup |= (pr[jj] == r);
-        if (dup) continue;
+        if (!((first >> j) & 1u)) continue;
       }
       u32x4* dst = send + (size_t)r * cpr;
 #pragma unroll
