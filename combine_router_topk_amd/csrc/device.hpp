@@ -140,6 +140,30 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
   return v;
 }
 
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> every lane of the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> every lane of rows 2 and 3
+
+// Row-masked DPP move: rows outside ROW_MASK receive 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_rows(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Max over the 64 lanes of a wave, returned as a wave-uniform value: a
+// butterfly inside each row of 16 lanes, then the row maxima are carried
+// forward with row broadcasts (rows 1 and 3 take rows 0 and 2, rows 2 and 3
+// take row 1), so lane 63 ends with the maximum.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax(v, dpp<kDppXor1>(v));
+  v = umax(v, dpp<kDppXor2>(v));
+  v = umax(v, dpp<kDppHalfMirror>(v));
+  v = umax(v, dpp<kDppMirror>(v));
+  v = umax(v, dpp_rows<kDppRowBcast15, 0xA>(v));
+  v = umax(v, dpp_rows<kDppRowBcast31, 0xC>(v));
+  return readlane(v, 63);
+}
+
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
   const uint64_t u = __double_as_longlong(x);
