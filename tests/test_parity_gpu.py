@@ -124,6 +124,21 @@ def test_random_replica_tables(order, seed):
     run_and_check(w, seed, flags=flags, rep=rep, order=order)
 
 
+@pytest.mark.parametrize("order", ["constrained", "id"])
+def test_random_replica_tables_more_than_64_gpus(order):
+    """128 virtual GPUs: the greedy keeps its counters in LDS rather than in
+    a register per lane."""
+    rng = np.random.default_rng(321)
+    E, R, maxrep = 256, 128, 3
+    rep = np.full((E, maxrep), -1, np.int32)
+    for e in range(E):
+        n = int(rng.integers(1, maxrep + 1))
+        rep[e, :n] = rng.choice(R, size=n, replace=False)
+    w = synth.Workload("rep_R128", 600, E, 8, 64, R, synth.BF16, "zipf1.0_perm", False)
+    flags = B.MOE_FLAG_GREEDY_ID_ORDER if order == "id" else 0
+    run_and_check(w, 4, flags=flags, rep=rep, order=order)
+
+
 def test_empty_batch():
     w = synth.Workload("empty", 0, 8, 2, 128, 4, synth.F16, "none", False)
     say("[case] empty batch")
