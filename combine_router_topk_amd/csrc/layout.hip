@@ -210,21 +210,29 @@ __global__ __launch_bounds__(kPlanThreads) void layout_plan_kernel(
   }
   if (tid == 0) rank_offsets[R] = total;
   __syncthreads();
-  if (tid < E) {
-    // rows of lower-id experts on the same rank, 8 LDS entries per step
-    int acc = 0;
-    const int e_pad = (E + 7) & ~7;
-    for (int b = 0; b < e_pad; b += 8) {
-      const int4 r0 = *reinterpret_cast<const int4*>(&s_rank[b]);
-      const int4 r1 = *reinterpret_cast<const int4*>(&s_rank[b + 4]);
-      const int4 c0 = *reinterpret_cast<const int4*>(&s_cnt[b]);
-      const int4 c1 = *reinterpret_cast<const int4*>(&s_cnt[b + 4]);
-      const int rr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-      const int cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  {
+    // rows of lower-id experts on the same rank: P adjacent threads per
+    // expert, each scanning every P-th group of 8 LDS entries, their partial
+    // sums then added with shuffles inside the wave (integer adds)
+    const int P = E <= 64 ? 16 : (E <= 128 ? 8 : (E <= 256 ? 4 : (E <= 512 ? 2 : 1)));
+    const int e = tid / P, q = tid % P;
+    int acc = 0, er = 0;
+    if (e < E) {
+      er = s_rank[e];
+      const int e_pad = (E + 7) & ~7;
+      for (int b = q * 8; b < e_pad; b += 8 * P) {
+        const int4 r0 = *reinterpret_cast<const int4*>(&s_rank[b]);
+        const int4 r1 = *reinterpret_cast<const int4*>(&s_rank[b + 4]);
+        const int4 c0 = *reinterpret_cast<const int4*>(&s_cnt[b]);
+        const int4 c1 = *reinterpret_cast<const int4*>(&s_cnt[b + 4]);
+        const int rr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+        const int cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc += (rr[i] == my_r && b + i < tid) ? cc[i] : 0;
+        for (int i = 0; i < 8; ++i) acc += (rr[i] == er && b + i < e) ? cc[i] : 0;
+      }
     }
-    expert_offsets[tid] = s_roff[my_r] + acc;
+    for (int off = P / 2; off > 0; off /= 2) acc += __shfl_xor(acc, off, P);
+    if (e < E && q == 0) expert_offsets[e] = s_roff[er] + acc;
   }
   if (ss_rank_offsets != nullptr) {
     // single-send rows: one per (token, rank), grouped by rank
