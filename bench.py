@@ -13,7 +13,8 @@ After the headline loop, and outside it, the same batch also times the
 single-send variant (layout, one-row-per-rank dispatch, receiver fan-out), the
 backward of the dispatch and the combine, and the routing statistics, and
 the replicated decode workload compares the greedy replica assignment with
-token-balanced routing; each is reported in its own object of the JSON line.
+token-balanced routing and times a decode step eager against a HIP graph
+replay; each is reported in its own object of the JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line.
@@ -53,6 +54,8 @@ def parse():
                     help="timed calls of the routing statistics after the headline loop (0 = skip)")
     ap.add_argument("--eplb-steps", type=int, default=20,
                     help="timed token-balanced splits on the replicated decode workload (0 = skip)")
+    ap.add_argument("--graph-steps", type=int, default=200,
+                    help="decode steps timed eager and as a HIP graph replay (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 30,
                     help="tokens in the oracle's CPU-baseline sample (0 = skip; default all)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -265,6 +268,36 @@ def eplb_leg(P, B, synth, np, torch, dev, steps, ev, seed):
             "max_pairs_per_gpu": {"greedy": g_tok, "token_balanced": e_tok}}
 
 
+def graph_leg(P, B, synth, np, torch, dev, steps, seed):
+    """The whole path on the replicated decode workload, where every kernel is
+    small and the host's launches set the pace: wall time per step for eager
+    calls against one replay of a HIP graph holding the same pass (warm
+    cache, the stream drained after each step in both cases)."""
+    w = synth.DECODE
+    logits, x = synth.make_logits(w, seed), synth.make_x(w, seed)
+    rep = synth.replica_table(w)
+    p = B.make_problem(w.T, w.E, w.k, w.H, w.R, w.act_dtype)
+    b = P.allocate(p, torch.from_numpy(logits), torch.from_numpy(x.view(np.int16)).view(torch.float16),
+                   torch.from_numpy(rep), device=dev)
+    g = P.capture(b)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+            torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+            torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e6
+
+    eager_us = timed(lambda: P.run(b))
+    graph_us = timed(g.replay)
+    return {"workload": w.name, "steps": steps, "eager_us_per_step": round(eager_us, 1),
+            "graph_us_per_step": round(graph_us, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -395,6 +428,8 @@ def main():
         res["routing_stats"] = stats_leg(P, w, b, args.stats_steps, ev, np, torch)
     if args.eplb_steps > 0:
         res["eplb"] = eplb_leg(P, B, synth, np, torch, dev, args.eplb_steps, ev, args.seed)
+    if args.graph_steps > 0:
+        res["decode_graph"] = graph_leg(P, B, synth, np, torch, dev, args.graph_steps, args.seed)
     if args.cpu_tokens > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_tokens, args.cpu_seconds)
     print(json.dumps(res), flush=True)

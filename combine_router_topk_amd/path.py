@@ -95,6 +95,26 @@ def run(b: Buffers, stream=None) -> None:
         step(b, stream)
 
 
+def capture(b: Buffers, steps=STEPS) -> torch.cuda.CUDAGraph:
+    """Records one pass of `steps` (the whole path by default) into a HIP
+    graph. The library only enqueues kernels (no memset, allocation or
+    synchronisation), so the pass replays with one launch; the buffers of `b`
+    are the graph's inputs and outputs: copy a new batch into b.logits / b.x
+    in place, then replay. One eager pass on a side stream comes first, as
+    torch asks before a capture."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for step in steps:
+            step(b)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for step in steps:
+            step(b)
+    return g
+
+
 @dataclass
 class SingleSend:
     """Single-send buffers: one row per (token, destination rank). The row
