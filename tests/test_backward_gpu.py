@@ -204,3 +204,25 @@ def test_backward_full_size(w):
         gg = g[t0:t0 + step].float()
         err = (dx[t0:t0 + step].float() - gg).abs()
         assert bool((err <= rel * gg.abs() + 2.0 ** -23).all()), t0
+
+
+def test_backward_deterministic_bitwise():
+    """dw and dx are fp32 sums in a fixed order: two runs give the same bits."""
+    w = synth.scaled(synth.TRAIN_TOP6, T=3000, H=520)
+    say("[case] backward determinism")
+    logits, x = synth.make_logits(w, 9), synth.make_x(w, 9)
+    b = run_gpu(w, logits, x, None)
+    p = B.make_problem(w.T, w.E, w.k, w.H, w.R, w.act_dtype, B.MOE_FLAG_OUT_F32)
+    g = bits_to_tensor(synth.make_grad(w, 9, w.T), w.act_dtype).cuda()
+    outs = []
+    for _ in range(2):
+        dy = torch.empty_like(b.y)
+        dw = torch.empty(w.T * w.k, dtype=torch.float32, device="cuda")
+        dx = torch.empty(w.T, w.H, dtype=torch.float32, device="cuda")
+        B.moe_combine_backward(p, g, b.y, b.pos, b.w, dy, dw)
+        B.moe_dispatch_backward(p, dy, b.pos, dx)
+        torch.cuda.synchronize()
+        outs.append((dy.view(torch.int16).clone(), dw.view(torch.int32).clone(),
+                     dx.view(torch.int32).clone()))
+    for a, c in zip(*outs):
+        assert torch.equal(a, c)
