@@ -27,6 +27,9 @@
 //     ids with one ballot per id bit and counting lower lanes; across the
 //     block's waves by per-wave counts in LDS; across rounds by running
 //     per-expert cursors. pos = cursor + rank, src[pos] = flat pair index.
+//  (4. layout_single_send, for the single-send rows.)
+// A small batch (T k <= 8192 pairs) runs all of it in one workgroup instead
+// (layout_small), sharing the same device functions.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -41,23 +44,13 @@ constexpr int kSegRegs = 48;  // rows per wave segment in the plan's column pass
 
 __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
-__global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
-    const int32_t* __restrict__ idx, int T, int E, int k, int R, int tpb,
-    const int32_t* __restrict__ assign, const int32_t* __restrict__ rep, int maxrep,
-    int32_t* __restrict__ hist, int32_t* __restrict__ ded, int32_t* __restrict__ lead_mask) {
-  extern __shared__ int smem[];
-  int* s_rank = smem;        // [E]
-  int* s_hist = smem + E;    // [E]
-  int* s_ded = smem + 2 * E; // [R]
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    s_rank[e] = expert_rank(e, E, R, assign, rep, maxrep);
-    s_hist[e] = 0;
-  }
-  for (int r = threadIdx.x; r < R; r += blockDim.x) s_ded[r] = 0;
-  __syncthreads();
-
-  const int t0 = blockIdx.x * tpb;
-  const int t1 = min(T, t0 + tpb);
+// Counts of tokens [t0, t1) into LDS: the selected experts (s_hist) and, per
+// token, its distinct destination ranks (s_ded); with lead_mask, bit j of
+// lead_mask[t] marks slot j as the token's first slot on its rank. All
+// threads of the block take part.
+__device__ void count_tokens(const int32_t* __restrict__ idx, int t0, int t1, int E, int k,
+                             const int* s_rank, int* s_hist, int* s_ded,
+                             int32_t* __restrict__ lead_mask) {
   const size_t i0 = (size_t)t0 * k, i1 = (size_t)t1 * k;
   for (size_t i = i0 + threadIdx.x; i < i1; i += blockDim.x)
     atomicAdd(&s_hist[clamp_expert(idx[i], E)], 1);
@@ -81,6 +74,24 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     }
     if (lead_mask != nullptr) lead_mask[t] = lead;
   }
+}
+
+__global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int R, int tpb,
+    const int32_t* __restrict__ assign, const int32_t* __restrict__ rep, int maxrep,
+    int32_t* __restrict__ hist, int32_t* __restrict__ ded, int32_t* __restrict__ lead_mask) {
+  extern __shared__ int smem[];
+  int* s_rank = smem;        // [E]
+  int* s_hist = smem + E;    // [E]
+  int* s_ded = smem + 2 * E; // [R]
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    s_rank[e] = expert_rank(e, E, R, assign, rep, maxrep);
+    s_hist[e] = 0;
+  }
+  for (int r = threadIdx.x; r < R; r += blockDim.x) s_ded[r] = 0;
+  __syncthreads();
+  const int t0 = blockIdx.x * tpb;
+  count_tokens(idx, t0, min(T, t0 + tpb), E, k, s_rank, s_hist, s_ded, lead_mask);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = s_hist[e];
   for (int r = threadIdx.x; r < R; r += blockDim.x) ded[(size_t)blockIdx.x * R + r] = s_ded[r];
@@ -165,35 +176,22 @@ __device__ int block_excl_scan(int v, int* s_wave, int* total) {
   return before + incl - v;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void layout_plan_kernel(
-    int T, int E, int k, int R, int nblk, int32_t* __restrict__ hist, int32_t* __restrict__ ded,
-    const int32_t* __restrict__ assign, const int32_t* __restrict__ rep, int maxrep,
-    int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
-    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ dedup,
-    int32_t* __restrict__ ss_rank_offsets) {
-  __shared__ __align__(16) int s_rank[kMaxE + 8];
-  __shared__ __align__(16) int s_cnt[kMaxE + 8];
-  __shared__ int s_ded[kMaxR];
-  __shared__ int s_rtok[kMaxR];
-  __shared__ int s_roff[kMaxR];
-  __shared__ int part[kPlanWaves][kWave];
-  __shared__ int s_wave[kPlanWaves];
-  __shared__ int s_wave2[kPlanWaves];
+// Everything the plan derives from the per-expert totals s_cnt, the dedup
+// totals s_ded and the expert ranks s_rank (each thread tid < E holds
+// s_rank[tid]; s_rtok zeroed): rank_of, per-rank row totals (LDS adds) and
+// their block scan (rank_offsets), dedup, each expert's offset (its rank's
+// offset plus the rows of lower-id experts on the same rank), and the
+// single-send rank offsets. s_rank and s_cnt must have room for E rounded up
+// to 8. Optional LDS copies: s_eoff[E] of the expert offsets, s_ssoff[R] of
+// the single-send offsets. All threads of the (1024-thread) block take part.
+__device__ void plan_finish(int E, int R, int* s_rank, int* s_cnt, const int* s_ded, int* s_rtok,
+                            int* s_roff, int* s_wave, int* s_wave2, int32_t* __restrict__ rank_of,
+                            int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_offsets,
+                            int32_t* __restrict__ dedup, int32_t* __restrict__ ss_rank_offsets,
+                            int* s_eoff, int* s_ssoff) {
   const int tid = threadIdx.x;  // E, R <= 1024 == blockDim.x: one expert / rank per thread
-  // issue the expert-rank loads now, use them after the column pass
-  int a_e = -1, p_e = 0;
   if (tid < E) {
-    if (assign != nullptr) a_e = assign[tid];
-    p_e = rep != nullptr ? rep[tid * maxrep] : tid / (E / R);
-  }
-  if (tid < R) s_rtok[tid] = 0;
-  column_pass(hist, E, ded, R, nblk, s_cnt, s_ded, part);  // ends with a barrier
-
-  int my_r = 0;
-  if (tid < E) {
-    my_r = a_e >= 0 ? a_e : p_e;
-    my_r = my_r < 0 ? 0 : (my_r >= R ? R - 1 : my_r);
-    s_rank[tid] = my_r;
+    const int my_r = s_rank[tid];
     rank_of[tid] = my_r;
     atomicAdd(&s_rtok[my_r], s_cnt[tid]);
   } else if (tid < ((E + 7) & ~7)) {
@@ -232,42 +230,64 @@ __global__ __launch_bounds__(kPlanThreads) void layout_plan_kernel(
       }
     }
     for (int off = P / 2; off > 0; off /= 2) acc += __shfl_xor(acc, off, P);
-    if (e < E && q == 0) expert_offsets[e] = s_roff[er] + acc;
+    if (e < E && q == 0) {
+      expert_offsets[e] = s_roff[er] + acc;
+      if (s_eoff != nullptr) s_eoff[e] = s_roff[er] + acc;
+    }
   }
   if (ss_rank_offsets != nullptr) {
     // single-send rows: one per (token, rank), grouped by rank
     int ss_total = 0;
     const int ss_off = block_excl_scan(tid < R ? s_ded[tid] : 0, s_wave2, &ss_total);
-    if (tid < R) ss_rank_offsets[tid] = ss_off;
+    if (tid < R) {
+      ss_rank_offsets[tid] = ss_off;
+      if (s_ssoff != nullptr) s_ssoff[tid] = ss_off;
+    }
     if (tid == 0) ss_rank_offsets[R] = ss_total;
   }
 }
 
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void layout_permute_kernel(
-    const int32_t* __restrict__ idx, int T, int E, int k, int tpb, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ expert_offsets, int32_t* __restrict__ pos,
-    int32_t* __restrict__ src) {
-  constexpr int kThreads = WAVES * kWave;
-  extern __shared__ int smem[];
-  int* run = smem;                   // [E] next free row of each expert
-  int* wcnt = smem + E;              // [WAVES][E] pairs per expert in a wave
-  int* wtag = smem + E + WAVES * E;  // [WAVES][E] round that wrote wcnt
-  const int b = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    run[e] = expert_offsets[e] + base[(size_t)b * E + e];
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) wtag[w * E + e] = 0;
-  }
-  __syncthreads();
+__global__ __launch_bounds__(kPlanThreads) void layout_plan_kernel(
+    int T, int E, int k, int R, int nblk, int32_t* __restrict__ hist, int32_t* __restrict__ ded,
+    const int32_t* __restrict__ assign, const int32_t* __restrict__ rep, int maxrep,
+    int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ dedup,
+    int32_t* __restrict__ ss_rank_offsets) {
+  __shared__ __align__(16) int s_rank[kMaxE + 8];
+  __shared__ __align__(16) int s_cnt[kMaxE + 8];
+  __shared__ int s_ded[kMaxR];
+  __shared__ int s_rtok[kMaxR];
+  __shared__ int s_roff[kMaxR];
+  __shared__ int part[kPlanWaves][kWave];
+  __shared__ int s_wave[kPlanWaves];
+  __shared__ int s_wave2[kPlanWaves];
+  const int tid = threadIdx.x;
+  // issue the expert-rank loads now, use them after the column pass
+  int my_r = 0;
+  if (tid < E) my_r = expert_rank(tid, E, R, assign, rep, maxrep);
+  if (tid < R) s_rtok[tid] = 0;
+  column_pass(hist, E, ded, R, nblk, s_cnt, s_ded, part);  // ends with a barrier
+  if (tid < E) s_rank[tid] = my_r;
+  plan_finish(E, R, s_rank, s_cnt, s_ded, s_rtok, s_roff, s_wave, s_wave2, rank_of,
+              expert_offsets, rank_offsets, dedup, ss_rank_offsets, nullptr, nullptr);
+}
 
+// Stable placement of the pairs [i0, i1), in order, after the running
+// per-expert cursors run[e]: inside a wave by matching expert ids with one
+// ballot per id bit and counting lower lanes, across the WAVES waves by
+// per-wave counts tagged by round in LDS (wcnt, wtag: [WAVES][E], wtag
+// zeroed), across rounds by advancing the cursors. pos = cursor + rank,
+// src[pos] = flat pair index. All WAVES * 64 threads take part; ends with a
+// barrier.
+template <int WAVES>
+__device__ void permute_rounds(const int32_t* __restrict__ idx, int64_t i0, int64_t i1, int E,
+                               int n_items, int* run, int* wcnt, int* wtag,
+                               int32_t* __restrict__ pos, int32_t* __restrict__ src) {
+  constexpr int kThreads = WAVES * kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
   const uint64_t lt = lanemask_lt(lane);
-  const int64_t i0 = (int64_t)b * tpb * k;
-  const int64_t i1 = min((int64_t)T * k, i0 + (int64_t)tpb * k);
-  const int n_items = T * k;
   int tag = 0;
   int e_next = (i0 + threadIdx.x < i1) ? idx[i0 + threadIdx.x] : 0;  // next round's expert, prefetched
   for (int64_t r0 = i0; r0 < i1; r0 += kThreads) {
@@ -303,6 +323,27 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_permute_kernel(
   }
 }
 
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void layout_permute_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int tpb, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ expert_offsets, int32_t* __restrict__ pos,
+    int32_t* __restrict__ src) {
+  extern __shared__ int smem[];
+  int* run = smem;                   // [E] next free row of each expert
+  int* wcnt = smem + E;              // [WAVES][E] pairs per expert in a wave
+  int* wtag = smem + E + WAVES * E;  // [WAVES][E] round that wrote wcnt
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    run[e] = expert_offsets[e] + base[(size_t)b * E + e];
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) wtag[w * E + e] = 0;
+  }
+  __syncthreads();
+  const int64_t i0 = (int64_t)b * tpb * k;
+  const int64_t i1 = min((int64_t)T * k, i0 + (int64_t)tpb * k);
+  permute_rounds<WAVES>(idx, i0, i1, E, T * k, run, wcnt, wtag, pos, src);
+}
+
 // Single-send rows: one per (token, destination rank), grouped by rank and
 // inside a rank by token. A token's leader slot for a rank (its first slot
 // on that rank) takes the next row of the rank; its other slots on the same
@@ -311,33 +352,15 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_permute_kernel(
 // leader's row is the number of leaders of its rank before it; a non-leader
 // sees its own leader among those before it, so its row is that count - 1.
 template <int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void layout_single_send_kernel(
-    const int32_t* __restrict__ idx, int T, int E, int k, int R, int tpb,
-    const int32_t* __restrict__ rank_of, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ ss_rank_offsets, const int32_t* __restrict__ lead_mask,
-    int32_t* __restrict__ ss_row, int32_t* __restrict__ ss_token) {
+__device__ void single_send_rounds(const int32_t* __restrict__ idx, int64_t i0, int64_t i1, int k,
+                                   int E, int R, int n_items, const int* s_rank, int* run,
+                                   int* wcnt, int* wtag, const int32_t* __restrict__ lead_mask,
+                                   int32_t* __restrict__ ss_row, int32_t* __restrict__ ss_token) {
   constexpr int kThreads = WAVES * kWave;
-  extern __shared__ int smem[];
-  int* s_rank = smem;                       // [E]
-  int* run = smem + E;                      // [R] next free single-send row of each rank
-  int* wcnt = smem + E + R;                 // [WAVES][R] leaders per rank in a wave
-  int* wtag = smem + E + R + WAVES * R;     // [WAVES][R] round that wrote wcnt
-  const int b = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) s_rank[e] = rank_of[e];
-  for (int r = threadIdx.x; r < R; r += blockDim.x) {
-    run[r] = ss_rank_offsets[r] + base[(size_t)b * R + r];
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) wtag[w * R + r] = 0;
-  }
-  __syncthreads();
-
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int nbits = R > 1 ? 32 - __builtin_clz((unsigned)(R - 1)) : 0;
   const uint64_t lt = lanemask_lt(lane);
-  const int64_t i0 = (int64_t)b * tpb * k;
-  const int64_t i1 = min((int64_t)T * k, i0 + (int64_t)tpb * k);
-  const int n_items = T * k;
   int tag = 0;
   for (int64_t r0 = i0; r0 < i1; r0 += kThreads) {
     ++tag;
@@ -375,6 +398,83 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_single_send_kernel(
   }
 }
 
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void layout_single_send_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int R, int tpb,
+    const int32_t* __restrict__ rank_of, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ ss_rank_offsets, const int32_t* __restrict__ lead_mask,
+    int32_t* __restrict__ ss_row, int32_t* __restrict__ ss_token) {
+  extern __shared__ int smem[];
+  int* s_rank = smem;                       // [E]
+  int* run = smem + E;                      // [R] next free single-send row of each rank
+  int* wcnt = smem + E + R;                 // [WAVES][R] leaders per rank in a wave
+  int* wtag = smem + E + R + WAVES * R;     // [WAVES][R] round that wrote wcnt
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_rank[e] = rank_of[e];
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    run[r] = ss_rank_offsets[r] + base[(size_t)b * R + r];
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) wtag[w * R + r] = 0;
+  }
+  __syncthreads();
+  const int64_t i0 = (int64_t)b * tpb * k;
+  const int64_t i1 = min((int64_t)T * k, i0 + (int64_t)tpb * k);
+  single_send_rounds<WAVES>(idx, i0, i1, k, E, R, T * k, s_rank, run, wcnt, wtag, lead_mask,
+                            ss_row, ss_token);
+}
+
+// The whole layout of a small batch (T k <= kSmallPairs) in one workgroup:
+// counts, plan, permutation and single-send rows, every table in LDS, with
+// the same device code as the multi-block kernels. A decode batch then
+// takes one launch instead of three or four.
+constexpr int kSmallPairs = 8192;
+
+__global__ __launch_bounds__(kPlanThreads) void layout_small_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int R,
+    const int32_t* __restrict__ assign, const int32_t* __restrict__ rep, int maxrep,
+    int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pos, int32_t* __restrict__ src,
+    int32_t* __restrict__ dedup, int32_t* __restrict__ ss_rank_offsets,
+    int32_t* __restrict__ ss_row, int32_t* __restrict__ ss_token, int32_t* __restrict__ lead) {
+  extern __shared__ __align__(16) int smem[];
+  __shared__ int s_wave[kPlanWaves];
+  __shared__ int s_wave2[kPlanWaves];
+  const int ep = (E + 8) & ~7;  // room for the plan's padding to a multiple of 8
+  const int M = E > R ? E : R;
+  int* s_rank = smem;            // [ep]
+  int* s_cnt = s_rank + ep;      // [ep]
+  int* s_ded = s_cnt + ep;       // [R]
+  int* s_rtok = s_ded + R;       // [R]
+  int* s_roff = s_rtok + R;      // [R]
+  int* s_ssoff = s_roff + R;     // [R]
+  int* run = s_ssoff + R;        // [M]
+  int* wcnt = run + M;           // [16][M]
+  int* wtag = wcnt + kPlanWaves * M;  // [16][M]
+  const bool ss = ss_rank_offsets != nullptr;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    s_rank[e] = expert_rank(e, E, R, assign, rep, maxrep);
+    s_cnt[e] = 0;
+  }
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    s_ded[r] = 0;
+    s_rtok[r] = 0;
+  }
+  __syncthreads();
+  count_tokens(idx, 0, T, E, k, s_rank, s_cnt, s_ded, ss ? lead : nullptr);
+  __syncthreads();
+  plan_finish(E, R, s_rank, s_cnt, s_ded, s_rtok, s_roff, s_wave, s_wave2, rank_of,
+              expert_offsets, rank_offsets, dedup, ss_rank_offsets, run, s_ssoff);
+  for (int i = threadIdx.x; i < kPlanWaves * E; i += blockDim.x) wtag[i] = 0;
+  __syncthreads();
+  permute_rounds<kPlanWaves>(idx, 0, (int64_t)T * k, E, T * k, run, wcnt, wtag, pos, src);
+  if (!ss) return;  // uniform: a kernel argument
+  for (int r = threadIdx.x; r < R; r += blockDim.x) run[r] = s_ssoff[r];
+  for (int i = threadIdx.x; i < kPlanWaves * R; i += blockDim.x) wtag[i] = 0;
+  __syncthreads();
+  single_send_rounds<kPlanWaves>(idx, 0, (int64_t)T * k, k, E, R, T * k, s_rank, run, wcnt, wtag,
+                                 lead, ss_row, ss_token);
+}
+
 }  // namespace
 
 hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const int32_t* assign,
@@ -388,6 +488,17 @@ hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const i
   int32_t* hist = ws;                                   // [nblk, E]
   int32_t* ded = ws + (size_t)bl.layout_nblk * E;       // [nblk, R]
   int32_t* lead = ded + (size_t)bl.layout_nblk * R;     // [T] leader masks (single-send)
+  {
+    const int ep = (E + 8) & ~7, M = E > R ? E : R;
+    const size_t small_ints = 2 * ep + 4 * R + (1 + 2 * kPlanWaves) * M;
+    // dynamic LDS under 64 KiB with room for the kernel's static 128 bytes
+    if (T > 0 && (int64_t)T * k <= kSmallPairs && small_ints <= 16 * 1024 - 64) {
+      layout_small_kernel<<<1, kPlanThreads, small_ints * sizeof(int), s>>>(
+          idx, T, E, k, R, assign, rep, maxrep, rank_of, expert_offsets, rank_offsets, pos, src,
+          dedup, ss_rank_offsets, ss_row, ss_token, lead);
+      return hipGetLastError();
+    }
+  }
   if (nblk > 0) {
     layout_count_kernel<<<nblk, kCountThreads, (2 * E + R) * sizeof(int), s>>>(
         idx, T, E, k, R, bl.layout_tpb, assign, rep, maxrep, hist, ded, ss ? lead : nullptr);
