@@ -95,3 +95,57 @@ def test_product_path_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\boracle\b", text), f
+
+
+def test_new_entry_points_reject_bad_arguments_before_any_launch():
+    p = prob()
+    ref = ctypes.byref(p)
+    lib = B._lib
+    fake = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    ws = 1 << 20
+    # single-send layout: a NULL single-send output, a short workspace
+    assert lib.moe_layout_single_send(ref, fake, None, None, 1, fake, fake, fake, fake, fake, fake,
+                                      None, fake, fake, fake, ws, None) == B.MOE_ERR_INVALID_ARG
+    assert "ss_rank_offsets" in B.moe_last_error()
+    assert lib.moe_layout_single_send(ref, fake, None, None, 1, fake, fake, fake, fake, fake, fake,
+                                      fake, fake, fake, fake, 16, None) == B.MOE_ERR_WORKSPACE
+    # single-send dispatch and fan-out: negative capacity, misaligned rows
+    assert lib.moe_single_send_dispatch(ref, fake, fake, fake, -1, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_single_send_dispatch(ref, mis, fake, fake, 8, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_single_send_expand(ref, fake, fake, fake, fake, fake, -1, fake, None) \
+        == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_single_send_expand(ref, fake, None, fake, fake, fake, 8, fake, None) \
+        == B.MOE_ERR_INVALID_ARG
+    # capacity 0 and T = 0 are no-ops
+    assert lib.moe_single_send_dispatch(ref, None, None, None, 0, None) == B.MOE_OK
+    # backward: both outputs NULL, y missing for dw, w missing for dy
+    assert lib.moe_combine_backward(ref, fake, fake, fake, fake, None, None, None) \
+        == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_backward(ref, fake, None, fake, fake, None, fake, None) \
+        == B.MOE_ERR_INVALID_ARG
+    assert "y" in B.moe_last_error()
+    assert lib.moe_combine_backward(ref, fake, fake, fake, None, fake, None, None) \
+        == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_backward(ref, fake, fake, mis, None) == B.MOE_ERR_INVALID_ARG
+    # statistics: the f64 output is required and 8-byte aligned
+    assert lib.moe_routing_stats(ref, fake, fake, fake, fake, None, None, None) \
+        == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_routing_stats(ref, fake, fake, fake, fake, None, mis, None) \
+        == B.MOE_ERR_INVALID_ARG
+    # token-balanced split: no table needs R | E; a table needs 1 <= maxrep <= 16
+    p2 = prob(E=12, R=5)
+    assert lib.moe_token_balanced_split(ctypes.byref(p2), fake, fake, fake, fake, None, 1, fake,
+                                        fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_token_balanced_split(ref, fake, fake, fake, fake, fake, 17, fake, fake, fake,
+                                        None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_new_entry_points_empty_batch_is_noop_where_nothing_is_written():
+    p = prob(T=0)
+    ref = ctypes.byref(p)
+    lib = B._lib
+    assert lib.moe_single_send_dispatch(ref, None, None, None, 4, None) == B.MOE_OK
+    assert lib.moe_single_send_expand(ref, None, None, None, None, None, 4, None, None) == B.MOE_OK
+    assert lib.moe_combine_backward(ref, None, None, None, None, None, None, None) == B.MOE_OK
+    assert lib.moe_dispatch_backward(ref, None, None, None, None) == B.MOE_OK
