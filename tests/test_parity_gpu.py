@@ -8,6 +8,7 @@ import torch
 import oracle
 import synth
 from combine_router_topk_amd import binding as B
+from combine_router_topk_amd import path as P
 from pathcheck import check_meta, check_rows, run_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -165,3 +166,30 @@ def test_binding_rejects_short_buffers_and_workspace():
     assert ei.value.status == B.MOE_ERR_WORKSPACE
     with pytest.raises(ValueError):
         B.moe_route(p, logits, idx[:10], wt, counts, small_ws)
+
+
+def test_two_streams_concurrently():
+    """Two batches on two streams at once (the library keeps no state
+    between calls): each must equal its own sequential run, bit for bit."""
+    say("[case] two streams")
+    ws_ = [synth.scaled(synth.TRAIN_TOP6, T=2500, H=256), synth.DECODE]
+    bufs, want = [], []
+    for w in ws_:
+        logits, x = synth.make_logits(w, 11), synth.make_x(w, 11)
+        rep = synth.replica_table(w)
+        b = run_gpu(w, logits, x, rep)                  # sequential reference
+        want.append({k: getattr(b, k).clone() for k in ("pos", "src", "send", "y", "out", "w")})
+        for k in ("pos", "src", "send", "y", "out", "w"):
+            getattr(b, k).zero_()
+        bufs.append(b)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):
+        for b, st in zip(bufs, streams):
+            with torch.cuda.stream(st):
+                P.run(b)
+        torch.cuda.synchronize()
+        for b, wnt in zip(bufs, want):
+            for k, v in wnt.items():
+                got = getattr(b, k)
+                assert torch.equal(got.contiguous().view(torch.uint8), v.contiguous().view(torch.uint8)), k
