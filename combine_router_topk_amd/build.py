@@ -50,5 +50,23 @@ def build(jobs: int = 8) -> str:
     return LIB
 
 
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "check_abi.c")
+C_CHECK_LIB = os.path.join(ROOT, "tests", "c_abi", "libcheck_abi.so")
+
+
+def build_c_check() -> str:
+    """The plain-C caller of the library used by the tests (gcc, C11): a
+    shared library with moe_c_abi_check(), found by the tests next to its
+    source; it finds libmoe_route.so through its run path."""
+    tmp = C_CHECK_LIB + ".tmp"
+    _run(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__",
+          "-I/opt/rocm/include", f"-I{INCLUDE}", C_CHECK_SRC, f"-L{PKG}", "-lmoe_route",
+          "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../combine_router_topk_amd",
+          "-Wl,-rpath,/opt/rocm/lib", "-o", tmp])
+    os.replace(tmp, C_CHECK_LIB)
+    return C_CHECK_LIB
+
+
 if __name__ == "__main__":
     print(build())
+    print(build_c_check())

@@ -11,13 +11,16 @@ GOLDEN = os.path.join(ROOT, "tests", "golden")
 LIB = os.path.join(ROOT, "combine_router_topk_amd", "libmoe_route.so")
 
 # Tests load what is built; they build only when nothing is.
-if not os.path.exists(LIB):
+C_CHECK_LIB = os.path.join(ROOT, "tests", "c_abi", "libcheck_abi.so")
+if not os.path.exists(LIB) or not os.path.exists(C_CHECK_LIB):
     import importlib.util
     _spec = importlib.util.spec_from_file_location(
         "_moe_build", os.path.join(ROOT, "combine_router_topk_amd", "build.py"))
     _mod = importlib.util.module_from_spec(_spec)
     _spec.loader.exec_module(_mod)
-    _mod.build()
+    if not os.path.exists(LIB):
+        _mod.build()
+    _mod.build_c_check()
 
 
 def pytest_configure(config):

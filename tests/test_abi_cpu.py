@@ -149,3 +149,9 @@ def test_new_entry_points_empty_batch_is_noop_where_nothing_is_written():
     assert lib.moe_single_send_expand(ref, None, None, None, None, None, 4, None, None) == B.MOE_OK
     assert lib.moe_combine_backward(ref, None, None, None, None, None, None, None) == B.MOE_OK
     assert lib.moe_dispatch_backward(ref, None, None, None, None) == B.MOE_OK
+
+
+def test_plain_c_caller_builds_and_exports_its_check():
+    from conftest import C_CHECK_LIB
+    lib = ctypes.CDLL(C_CHECK_LIB)
+    assert hasattr(lib, "moe_c_abi_check")
