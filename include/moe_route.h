@@ -3,7 +3,10 @@
  * Instinct MI355X (gfx950): router top-k with gate weights, the expert demand
  * vector, METRO-style greedy replica assignment, the rank-grouped dispatch
  * layout with single-send dedup counts, the row dispatch, an expert stand-in,
- * and the weighted combine.
+ * and the weighted combine; around them, single-send dispatch (one row per
+ * token and destination rank) with its receiver fan-out, the backward of the
+ * combine and the dispatch, routing statistics, and token-balanced replica
+ * routing as the greedy's baseline.
  *
  * Sources (web pages on MoE dispatch and combine):
  *   [METRO]  "METRO AllGather vs AllToAll for MoE decode" (fanout.sh).
@@ -95,9 +98,10 @@ const char* moe_status_string(int32_t status);
 /* Description of the last non-OK status returned on this thread ("" if none). */
 const char* moe_last_error(void);
 
-/* Bytes of device workspace moe_route and moe_layout need for this problem
- * (one buffer of this size serves both; its contents need no initialisation
- * and are not meaningful between calls). Host only; enqueues nothing. */
+/* Bytes of device workspace moe_route, moe_layout and moe_layout_single_send
+ * need for this problem (one buffer of this size serves all three; its
+ * contents need no initialisation and are not meaningful between calls).
+ * Host only; enqueues nothing. */
 moe_status moe_workspace_bytes(const moe_problem* p, size_t* bytes);
 
 /* Router top-k, gate weights and the global expert demand vector.
