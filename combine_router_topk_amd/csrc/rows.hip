@@ -1,5 +1,7 @@
 // Row movement: dispatch of token rows into the rank-grouped send buffer, the
-// expert stand-in, and the weighted combine back to token order.
+// expert stand-in, and the weighted combine back to token order; also the
+// single-send dispatch (one row per token and destination rank) and its
+// receiver fan-out back to the expert-grouped rows.
 //
 // "METRO AllGather vs AllToAll for MoE decode", section "Work the 8-GPU
 // payload example" (the dispatch payload is token activation rows) and
@@ -8,7 +10,7 @@
 // expert placement and token shuffling, section "Why communication is the
 // target" (each layer dispatches tokens and combines results).
 //
-// All three are HBM-bound streams of 16-byte chunks. A row is split over a
+// All are HBM-bound streams of 16-byte chunks. A row is split over a
 // team of TPT lanes (TPT a power of two, up to the 256-thread block); small
 // rows pack several tokens into one block. Each lane issues all of its loads
 // before its stores or arithmetic so many 16-byte requests are in flight.
