@@ -43,7 +43,8 @@ moe_status check_problem(const moe_problem* p, const char* fn) {
   if (p->act_dtype != MOE_F16 && p->act_dtype != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "%s: act_dtype=%d is neither MOE_F16 nor MOE_BF16", fn, p->act_dtype);
   if (p->flags & ~kKnownFlags) return fail(MOE_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", fn, p->flags & ~kKnownFlags);
-  if ((int64_t)p->T * p->k > INT32_MAX) return fail(MOE_ERR_INVALID_ARG, "%s: T*k exceeds 2^31-1", fn);
+  if ((int64_t)p->T * p->k > MOE_MAX_ROWS)
+    return fail(MOE_ERR_INVALID_ARG, "%s: T*k=%lld exceeds %d", fn, (long long)p->T * p->k, MOE_MAX_ROWS);
   return MOE_OK;
 }
 

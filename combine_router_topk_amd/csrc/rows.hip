@@ -395,12 +395,14 @@ hipError_t launch_single_send_expand(const void* send_ss, const int32_t* ss_rank
   const u32x4* in = static_cast<const u32x4*>(send_ss);
   u32x4* out = static_cast<u32x4*>(send);
   const int32_t* n_ss = ss_rank_offsets + R;
+  // there are at most T*k single-send rows, so blocks past that would only exit
+  const int grid = ss_capacity < T * k ? ss_capacity : T * k;
   if (cpr <= 256)
-    fanout_kernel<kRowThreads, 1><<<ss_capacity, kRowThreads, 0, s>>>(in, n_ss, ss_token, ss_row,
-                                                                     pos, out, T, k, cpr);
+    fanout_kernel<kRowThreads, 1><<<grid, kRowThreads, 0, s>>>(in, n_ss, ss_token, ss_row, pos,
+                                                              out, T, k, cpr);
   else
-    fanout_kernel<kRowThreads, 2><<<ss_capacity, kRowThreads, 0, s>>>(in, n_ss, ss_token, ss_row,
-                                                                     pos, out, T, k, cpr);
+    fanout_kernel<kRowThreads, 2><<<grid, kRowThreads, 0, s>>>(in, n_ss, ss_token, ss_row, pos,
+                                                              out, T, k, cpr);
   return hipGetLastError();
 }
 

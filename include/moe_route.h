@@ -72,10 +72,14 @@ enum {
 };
 
 /* Limits checked on the host. */
-enum { MOE_MAX_E = 1024, MOE_MAX_K = 16, MOE_MAX_R = 1024, MOE_MAX_REP = 16 };
+/* MOE_MAX_ROWS bounds T*k: kernels that give each send row a 256-thread
+ * block launch up to T*k blocks, and one launch holds fewer than 2^32
+ * work-items. */
+enum { MOE_MAX_E = 1024, MOE_MAX_K = 16, MOE_MAX_R = 1024, MOE_MAX_REP = 16,
+       MOE_MAX_ROWS = (1 << 24) - 1 };
 
 /* One routing problem.
- *   T  tokens, T >= 0, T*k < 2^31
+ *   T  tokens, T >= 0, T*k <= MOE_MAX_ROWS (2^24 - 1)
  *   E  experts, 1 <= E <= 1024
  *   k  experts selected per token, 1 <= k <= min(E, 16)
  *   H  hidden width (elements per activation row), H > 0, H % 8 == 0

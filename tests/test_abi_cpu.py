@@ -43,12 +43,21 @@ def prob(**kw):
 @pytest.mark.parametrize("bad", [dict(T=-1), dict(E=0), dict(E=1025), dict(k=0), dict(k=9),
                                  dict(E=32, k=17), dict(H=12), dict(H=0), dict(R=0),
                                  dict(R=1025), dict(act_dtype=3), dict(flags=1 << 7),
-                                 dict(T=1 << 30, k=4)])
+                                 dict(T=1 << 30, k=4), dict(T=1 << 23, k=2)])
 def test_invalid_problems_rejected(bad):
     n = ctypes.c_size_t(0)
     st = B._lib.moe_workspace_bytes(ctypes.byref(prob(**bad)), ctypes.byref(n))
     assert st == B.MOE_ERR_INVALID_ARG, (bad, B.moe_last_error())
     assert B.moe_last_error()
+
+
+def test_row_limit_is_inclusive():
+    """T*k up to 2^24 - 1 is accepted: a one-block-per-row launch of that many
+    256-thread blocks stays under 2^32 work-items."""
+    n = ctypes.c_size_t(0)
+    for T, k in (((1 << 24) - 1, 1), ((1 << 23) - 1, 2)):
+        assert B._lib.moe_workspace_bytes(ctypes.byref(prob(T=T, k=k)), ctypes.byref(n)) == B.MOE_OK
+        assert n.value > 0
 
 
 def test_workspace_size_grows_with_tokens():
