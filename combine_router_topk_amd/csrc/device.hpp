@@ -74,6 +74,15 @@ __device__ __forceinline__ float keep_f32(float v) {
   return v;
 }
 
+// Declares the launch's dynamic LDS so that a launch can reserve some: the
+// runtime allocates dynamic LDS only for a kernel that references it. The
+// reservation is never read or written (never_negative is a row length); it
+// only caps how many blocks share a CU's 160 KiB of LDS.
+__device__ __forceinline__ void declare_lds_reserve(int never_negative) {
+  extern __shared__ int lds_reserve[];
+  if (never_negative < 0) lds_reserve[threadIdx.x] = 0;
+}
+
 // ---- order-preserving keys for top-k ---------------------------------------
 // Larger key = better logit. Finite values and +-inf map monotonically into
 // [0x007fffff, 0xff800000]; -0.0 is folded onto +0.0 so the two tie; any NaN

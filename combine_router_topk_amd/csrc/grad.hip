@@ -188,6 +188,7 @@ template <int ACT, int KMAX, bool OUT_F32, bool ONE>
 __global__ __launch_bounds__(kGradThreads) void dispatch_backward_kernel(
     const u32x4* __restrict__ dsend, const int32_t* __restrict__ pos, void* __restrict__ dx, int T,
     int k, int cpr, int tpt) {
+  declare_lds_reserve(cpr);
   int t, lt, stride;
   grad_team<ONE>(tpt, t, lt, stride);
   if (t >= T) return;
@@ -262,11 +263,22 @@ hipError_t launch_cb_k(const u32x4* dout, const u32x4* y, const int32_t* pos, co
   return launch_cb<ACT, 16>(dout, y, pos, w, dy, dw, T, k, cpr, s);
 }
 
+// LDS reservation of the one-row dispatch backward (see if_many_blocks),
+// from cold-cache sweeps on MI355X over H = 2048, 4096, 7168 and k = 2..8:
+// rows over 256 chunks take 48 KiB at k = 3..4 (6-12% over none) and 32 KiB
+// otherwise (7-9% at H = 7168, 1.5-7% at H = 4096); rows of 256 chunks or
+// fewer were fastest with none.
+size_t dispatch_backward_reserve(int k, int cpr) {
+  if (cpr <= 256) return 0;
+  return (k >= 3 && k <= 4 ? 48 : 32) * kKiB;
+}
+
 template <int ACT, int KMAX, bool OUT_F32>
 hipError_t launch_db(const u32x4* dsend, const int32_t* pos, void* dx, int T, int k, int cpr,
                      hipStream_t s) {
   if (cpr >= kGradOneRowChunks) {
-    dispatch_backward_kernel<ACT, KMAX, OUT_F32, true><<<T, kGradThreads, 0, s>>>(
+    const size_t res = if_many_blocks(dispatch_backward_reserve(k, cpr), T);
+    dispatch_backward_kernel<ACT, KMAX, OUT_F32, true><<<T, kGradThreads, res, s>>>(
         dsend, pos, dx, T, k, cpr, kGradThreads);
   } else {
     const int tpt = grad_threads_per_row(cpr);

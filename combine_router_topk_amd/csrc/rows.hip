@@ -61,10 +61,7 @@ template <int NT, int U, bool ONE, bool SERIAL = false, bool SS = false>
 __global__ __launch_bounds__(NT) void dispatch_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ send, int T,
     int k, int cpr, int tpt, int capacity = 0) {
-  // Dynamic LDS is only allocated for a kernel that declares it; the launch
-  // may reserve some here to cap how many blocks share a CU. Never accessed.
-  extern __shared__ int occupancy_reserve[];
-  if (cpr < 0) occupancy_reserve[threadIdx.x] = 0;
+  declare_lds_reserve(cpr);
   int t, lt, stride;
   row_team<NT, ONE>(tpt, t, lt, stride);
   if (t >= T) return;
@@ -113,6 +110,7 @@ __global__ __launch_bounds__(kRowThreads) void standin_kernel(
     const u32x4* send, const int32_t* __restrict__ src, const int32_t* __restrict__ idx, u32x4* y,
     int n, int E, int cpr, int tpt) {  // y may alias send: each chunk is read, then written, by one lane
   int r, lt, stride;
+  declare_lds_reserve(cpr);
   row_team<kRowThreads, ONE>(tpt, r, lt, stride);
   if (r >= n) return;
   const int sr = src[r];
@@ -158,6 +156,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
     void* __restrict__ out, int T, int k_rt, int cpr, int tpt) {
   const int k = EXACT ? KMAX : k_rt;
   int t, lt, stride;
+  declare_lds_reserve(cpr);
   row_team<kRowThreads, ONE>(tpt, t, lt, stride);
   if (t >= T) return;
   size_t row[KMAX];
@@ -247,6 +246,7 @@ __global__ __launch_bounds__(NT) void fanout_kernel(
     const u32x4* __restrict__ send_ss, const int32_t* __restrict__ n_ss_ptr,
     const int32_t* __restrict__ ss_token, const int32_t* __restrict__ ss_row,
     const int32_t* __restrict__ pos, u32x4* __restrict__ send, int T, int k, int cpr) {
+  declare_lds_reserve(cpr);
   const int q = blockIdx.x;
   if (q >= *n_ss_ptr) return;
   const int t = ss_token[q];
@@ -285,11 +285,58 @@ int threads_per_row(int cpr) {
   return tpt;
 }
 
+// LDS reservations (see declare_lds_reserve): fewer resident blocks per CU
+// mean fewer concurrent scattered row streams, which the memory system
+// serves faster once each block keeps enough bytes in flight. A CU then
+// holds at most 160 KiB / reservation blocks, fewer where registers bind
+// first (32 and 40 KiB measured alike). The values below come from
+// cold-cache sweeps on MI355X of
+// every one-row kernel over H = 2048, 4096, 7168 and k = 2..8 (reservations
+// 0 to 64 KiB); each rule names the measured gain over no reservation.
+
+// Dispatch (plain and single-send): rows over 512 chunks use 128-thread
+// blocks, best with 24 KiB at k <= 2 and 32 KiB above (H = 7168: 5-8%);
+// 257-512 chunks with k >= 4: 64 KiB (H = 4096, k = 4: 9%); otherwise 48 KiB
+// (H = 4096, k = 2: 71 vs 81 us; H = 2048, k = 6: 86 vs 93 us).
+size_t dispatch_reserve(int k, int cpr) {
+  if (cpr > 512) return (k <= 2 ? 24 : 32) * kKiB;
+  if (cpr > 256 && k >= 4) return 64 * kKiB;
+  return 48 * kKiB;
+}
+
+// Blocks of a dispatch launch: one row each, or several rows under 64 chunks.
+long long dispatch_blocks(int T, int cpr) {
+  if (cpr >= kOneRowChunks) return T;
+  const int per_blk = kRowThreads / threads_per_row(cpr);
+  return (T + per_blk - 1) / per_blk;
+}
+
+// Stand-in: rows over 512 chunks, 24 KiB (H = 7168: 5-12%); shorter rows
+// were fastest with none.
+size_t standin_reserve(int cpr) { return cpr > 512 ? 24 * kKiB : 0; }
+
+// Fan-out, two chunks per lane (rows over 256 chunks): 32 KiB at every k
+// measured (6-15%); rows of 256 chunks or fewer were fastest with none.
+size_t fanout_reserve(int cpr) { return cpr > 256 ? 32 * kKiB : 0; }
+
+// Combine, batched shape (rows over 256 chunks, k <= 8): the row loads in
+// flight per block grow with k, so the best block count falls with k:
+// k >= 6: 64 KiB (6-9%); k = 3..5: 48 KiB (6%); k <= 2: 32 KiB for rows over
+// 512 chunks (7%), none for shorter rows. The one-chunk shape (rows of
+// 64-256 chunks) was fastest with none.
+size_t combine_reserve(int k, int cpr) {
+  if (cpr <= kRowThreads || k > 8) return 0;
+  if (k >= 6) return 64 * kKiB;
+  if (k >= 3) return 48 * kKiB;
+  return cpr > 512 ? 32 * kKiB : 0;
+}
+
 template <int ACT, bool OUT_F32, bool ONE>
 hipError_t launch_combine_k(const u32x4* y, const int32_t* pos, const float* w, void* out, int T,
                             int k, int cpr, int tpt, int grid, hipStream_t s) {
+  const size_t res = ONE ? if_many_blocks(combine_reserve(k, cpr), grid) : 0;
 #define MOE_COMBINE(KM, ONE_, U, EX) \
-  combine_kernel<ACT, KM, OUT_F32, ONE_, U, EX><<<grid, kRowThreads, 0, s>>>(y, pos, w, out, T, k, cpr, tpt)
+  combine_kernel<ACT, KM, OUT_F32, ONE_, U, EX><<<grid, kRowThreads, res, s>>>(y, pos, w, out, T, k, cpr, tpt)
   if (ONE && cpr > kRowThreads && k <= 8) {  // the batched shape, exact k
     switch (k) {
       case 1: MOE_COMBINE(1, true, 2, true); break;
@@ -327,14 +374,11 @@ hipError_t launch_combine_a(const u32x4* y, const int32_t* pos, const float* w, 
 
 // Launch shape of the dispatch, from measurements on MI355X (cold cache):
 //  - rows of at most 512 chunks (H <= 4096): 256-thread blocks, one row per
-//    block (several for rows under 64 chunks), and a 48 KiB LDS reservation
-//    that the kernel never touches, so at most 3 blocks share a CU. Fewer concurrent
-//    scattered row streams wrote ~10% faster than full occupancy (H = 4096,
-//    k = 2: 71 vs 80 us; H = 2048, k = 6: 86 vs 97 us).
+//    block (several for rows under 64 chunks);
 //  - longer rows (H = 7168): 128-thread blocks with ceil(cpr / 128) chunks
-//    per lane at full occupancy and serialized row loads, which measured
-//    best there (1.63 ms against 1.69-1.77 ms for the other shapes).
-constexpr size_t kDispatchLdsReserve = 48 * 1024;
+//    per lane and serialized row loads (1.63 ms against 1.69-1.77 ms for
+//    256-thread shapes at full occupancy);
+//  - the LDS reservation of dispatch_reserve in both cases.
 
 hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T, int k, int H,
                            hipStream_t s) {
@@ -342,7 +386,7 @@ hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T,
   const int cpr = H / 8;
   const u32x4* xv = static_cast<const u32x4*>(x);
   u32x4* sv = static_cast<u32x4*>(send);
-  const size_t res = kDispatchLdsReserve;
+  const size_t res = if_many_blocks(dispatch_reserve(k, cpr), dispatch_blocks(T, cpr));
   if (cpr < kOneRowChunks) {
     const int tpt = threads_per_row(cpr);
     const int per_blk = kRowThreads / tpt;
@@ -355,10 +399,10 @@ hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T,
   } else {
     // ceil(cpr / 128) chunks per lane (a loop covers rows beyond 8 * 128)
     const int u = (cpr + 127) / 128;
-    if (u <= 5) dispatch_kernel<128, 5, true, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
-    else if (u == 6) dispatch_kernel<128, 6, true, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
-    else if (u == 7) dispatch_kernel<128, 7, true, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
-    else dispatch_kernel<128, 8, true, true><<<T, 128, 0, s>>>(xv, pos, sv, T, k, cpr, 0);
+    if (u <= 5) dispatch_kernel<128, 5, true, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
+    else if (u == 6) dispatch_kernel<128, 6, true, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
+    else if (u == 7) dispatch_kernel<128, 7, true, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
+    else dispatch_kernel<128, 8, true, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
   }
   return hipGetLastError();
 }
@@ -369,7 +413,7 @@ hipError_t launch_single_send_dispatch(const void* x, const int32_t* ss_row, voi
   const int cpr = H / 8;
   const u32x4* xv = static_cast<const u32x4*>(x);
   u32x4* sv = static_cast<u32x4*>(send_ss);
-  const size_t res = kDispatchLdsReserve;
+  const size_t res = if_many_blocks(dispatch_reserve(k, cpr), dispatch_blocks(T, cpr));
   const int cap = ss_capacity;
   if (cpr < kOneRowChunks) {
     const int tpt = threads_per_row(cpr);
@@ -381,7 +425,7 @@ hipError_t launch_single_send_dispatch(const void* x, const int32_t* ss_row, voi
   } else if (cpr <= 512) {
     dispatch_kernel<kRowThreads, 2, true, false, true><<<T, kRowThreads, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
   } else {
-    dispatch_kernel<128, 8, true, true, true><<<T, 128, 0, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
+    dispatch_kernel<128, 8, true, true, true><<<T, 128, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
   }
   return hipGetLastError();
 }
@@ -397,12 +441,13 @@ hipError_t launch_single_send_expand(const void* send_ss, const int32_t* ss_rank
   const int32_t* n_ss = ss_rank_offsets + R;
   // there are at most T*k single-send rows, so blocks past that would only exit
   const int grid = ss_capacity < T * k ? ss_capacity : T * k;
+  const size_t res = if_many_blocks(fanout_reserve(cpr), grid);
   if (cpr <= 256)
-    fanout_kernel<kRowThreads, 1><<<grid, kRowThreads, 0, s>>>(in, n_ss, ss_token, ss_row, pos,
-                                                              out, T, k, cpr);
+    fanout_kernel<kRowThreads, 1><<<grid, kRowThreads, res, s>>>(in, n_ss, ss_token, ss_row, pos,
+                                                                out, T, k, cpr);
   else
-    fanout_kernel<kRowThreads, 2><<<grid, kRowThreads, 0, s>>>(in, n_ss, ss_token, ss_row, pos,
-                                                              out, T, k, cpr);
+    fanout_kernel<kRowThreads, 2><<<grid, kRowThreads, res, s>>>(in, n_ss, ss_token, ss_row, pos,
+                                                                out, T, k, cpr);
   return hipGetLastError();
 }
 
@@ -414,8 +459,9 @@ hipError_t launch_standin(const void* send, const int32_t* src, const int32_t* i
   const u32x4* in = static_cast<const u32x4*>(send);
   u32x4* out = static_cast<u32x4*>(y);
   if (cpr >= kOneRowChunks) {
-    if (act == 1) standin_kernel<1, true><<<n, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, 0);
-    else standin_kernel<2, true><<<n, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, 0);
+    const size_t res = if_many_blocks(standin_reserve(cpr), n);
+    if (act == 1) standin_kernel<1, true><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
+    else standin_kernel<2, true><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
   } else {
     const int tpt = threads_per_row(cpr);
     const int per_blk = kRowThreads / tpt;
