@@ -16,10 +16,10 @@
 // Three kernels:
 //  1. stats_zero: clears S and C (a fill kernel, so a captured graph holds
 //     no memset node).
-//  2. stats_count: one token per thread; S and C are counted in LDS when they
-//     fit (then added to the global matrices once per block), otherwise with
-//     integer atomics straight into the global matrices. Integer adds commute,
-//     so the counts do not depend on the order.
+//  2. stats_count: one token per thread over a grid of token chunks by row
+//     slices of C; each block counts its slice of C in LDS and adds it to C
+//     once; S is counted in LDS when it fits (else with atomics straight into
+//     S). Integer adds commute, so the counts do not depend on the order.
 //  3. stats_finalize (one workgroup): the expert maximum, the per-rank loads
 //     (column sums of S), the trace, and the Gini and Dirichlet sums, all in
 //     exact 64-bit integers; then a handful of fp64 operations for the four
@@ -35,7 +35,10 @@ namespace {
 
 constexpr int kStatThreads = 256;
 constexpr int kFinalThreads = 1024;
-constexpr int kLdsMatrixInts = 7936;  // a matrix up to this size is counted in LDS
+constexpr int kLdsMatrixInts = 7936;  // S up to this size is counted in LDS
+constexpr int kSliceInts = 8192;      // LDS ints of one row slice of C (32 KiB) at most
+constexpr int kCountLdsInts = 16384;  // the count kernel's LDS (64 KiB) at most
+constexpr int kCountBlocks = 1024;    // target grid size of the count kernel
 
 __global__ __launch_bounds__(kStatThreads) void stats_zero_kernel(int32_t* __restrict__ S, int64_t nS,
                                                                  int32_t* __restrict__ C, int64_t nC) {
@@ -47,37 +50,48 @@ __global__ __launch_bounds__(kStatThreads) void stats_zero_kernel(int32_t* __res
 
 __device__ __forceinline__ int clamp_id(int v, int n) { return v < 0 ? 0 : (v >= n ? n - 1 : v); }
 
-template <bool S_LDS, bool C_LDS>
+// Blocks form a grid of token chunks (x) by row slices of C (y): block
+// (x, y) reads the tokens of chunk x and counts, in LDS, the pairs whose
+// smaller expert a lies in slice y (a0 <= a < a0 + rows), so every slice of
+// C fits in LDS whatever E is; the slice's nonzero cells are then added to
+// C once per block. Blocks of slice 0 also count S (in LDS when it fits,
+// else with atomics straight into S).
+template <bool S_LDS>
 __global__ __launch_bounds__(kStatThreads) void stats_count_kernel(
-    const int32_t* __restrict__ idx, int T, int E, int k, int R, int tpb,
+    const int32_t* __restrict__ idx, int T, int E, int k, int R, int tpb, int slice_rows,
     const int32_t* __restrict__ rank_of, int32_t* __restrict__ S, int32_t* __restrict__ C) {
   extern __shared__ int smem[];
   int* s_rank = smem;                              // [E]
   int* s_S = smem + E;                             // [R*R] when S_LDS
-  int* s_C = s_S + (S_LDS ? R * R : 0);            // [E*E] when C_LDS
+  int* s_C = s_S + (S_LDS ? R * R : 0);            // [slice_rows*E] when C is counted
+  const bool do_s = blockIdx.y == 0;
   const bool do_c = C != nullptr;
+  const int a0 = blockIdx.y * slice_rows;
+  const int rows = min(slice_rows, E - a0);
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_rank[e] = clamp_id(rank_of[e], R);
   if constexpr (S_LDS)
-    for (int i = threadIdx.x; i < R * R; i += blockDim.x) s_S[i] = 0;
-  if constexpr (C_LDS)
-    if (do_c)
-      for (int i = threadIdx.x; i < E * E; i += blockDim.x) s_C[i] = 0;
+    if (do_s)
+      for (int i = threadIdx.x; i < R * R; i += blockDim.x) s_S[i] = 0;
+  if (do_c)
+    for (int i = threadIdx.x; i < rows * E; i += blockDim.x) s_C[i] = 0;
   __syncthreads();
 
   const int t0 = blockIdx.x * tpb;
   const int t1 = min(T, t0 + tpb);
   for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
-    const int src = static_cast<int>((int64_t)t * R / T);
     const int32_t* row = idx + (size_t)t * k;
     int e[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) e[j] = j < k ? clamp_id(row[j], E) : 0;
+    if (do_s) {
+      const int src = static_cast<int>((int64_t)t * R / T);
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k) {
-        const int cell = src * R + s_rank[e[j]];
-        if constexpr (S_LDS) atomicAdd(&s_S[cell], 1);
-        else atomicAdd(&S[cell], 1);
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j < k) {
+          const int cell = src * R + s_rank[e[j]];
+          if constexpr (S_LDS) atomicAdd(&s_S[cell], 1);
+          else atomicAdd(&S[cell], 1);
+        }
       }
     }
     if (do_c) {
@@ -86,26 +100,23 @@ __global__ __launch_bounds__(kStatThreads) void stats_count_kernel(
 #pragma unroll
         for (int j = i + 1; j < kMaxK; ++j) {
           if (j < k) {
-            const int a = min(e[i], e[j]), b = max(e[i], e[j]);
-            if (a != b) {  // equal only for out-of-range ids clamped to one value
-              if constexpr (C_LDS) atomicAdd(&s_C[a * E + b], 1);
-              else atomicAdd(&C[(size_t)a * E + b], 1);
-            }
+            const int a = min(e[i], e[j]) - a0, b = max(e[i], e[j]);
+            // a + a0 == b only for out-of-range ids clamped to one value
+            if (static_cast<unsigned>(a) < static_cast<unsigned>(rows) && a + a0 != b)
+              atomicAdd(&s_C[a * E + b], 1);
           }
         }
       }
     }
   }
-  if constexpr (S_LDS || C_LDS) {
-    __syncthreads();
-    if constexpr (S_LDS)
+  __syncthreads();
+  if constexpr (S_LDS)
+    if (do_s)
       for (int i = threadIdx.x; i < R * R; i += blockDim.x)
         if (s_S[i] != 0) atomicAdd(&S[i], s_S[i]);
-    if constexpr (C_LDS)
-      if (do_c)
-        for (int i = threadIdx.x; i < E * E; i += blockDim.x)
-          if (s_C[i] != 0) atomicAdd(&C[i], s_C[i]);
-  }
+  if (do_c)
+    for (int i = threadIdx.x; i < rows * E; i += blockDim.x)
+      if (s_C[i] != 0) atomicAdd(&C[(size_t)a0 * E + i], s_C[i]);
 }
 
 __device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* s_red) {
@@ -203,21 +214,24 @@ hipError_t launch_routing_stats(const int32_t* idx, const int32_t* rank_of, cons
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (T > 0) {
-    // about 256 blocks, whole multiples of the block size in tokens
-    int tpb = (T + 255) / 256;
-    tpb = ((tpb + kStatThreads - 1) / kStatThreads) * kStatThreads;
-    const int nblk = (T + tpb - 1) / tpb;
+    // C in row slices of at most kSliceInts ints (all of C in one slice when
+    // it fits), within kCountLdsInts together with the rank table and S
+    // (with E <= 1024 and S <= kLdsMatrixInts at least 7 rows remain); about
+    // kCountBlocks blocks, token chunks whole multiples of the block size
     const bool s_lds = nS <= kLdsMatrixInts;
-    const bool c_lds = C != nullptr && nC <= kLdsMatrixInts;
-    const size_t lds = (E + (s_lds ? nS : 0) + (c_lds ? nC : 0)) * sizeof(int);
-    if (s_lds && c_lds)
-      stats_count_kernel<true, true><<<nblk, kStatThreads, lds, s>>>(idx, T, E, k, R, tpb, rank_of, S, C);
-    else if (s_lds)
-      stats_count_kernel<true, false><<<nblk, kStatThreads, lds, s>>>(idx, T, E, k, R, tpb, rank_of, S, C);
-    else if (c_lds)
-      stats_count_kernel<false, true><<<nblk, kStatThreads, lds, s>>>(idx, T, E, k, R, tpb, rank_of, S, C);
+    const int slice_ints = std::min<int64_t>(kSliceInts, kCountLdsInts - E - (s_lds ? nS : 0));
+    const int slice_rows = C != nullptr ? std::max(1, std::min(E, slice_ints / E)) : E;
+    const int nslice = C != nullptr ? (E + slice_rows - 1) / slice_rows : 1;
+    const int nchunk_want = std::max(1, kCountBlocks / nslice);
+    int tpb = (T + nchunk_want - 1) / nchunk_want;
+    tpb = ((tpb + kStatThreads - 1) / kStatThreads) * kStatThreads;
+    const int nchunk = (T + tpb - 1) / tpb;
+    const size_t lds = (E + (s_lds ? nS : 0) + (C != nullptr ? (int64_t)slice_rows * E : 0)) * sizeof(int);
+    const dim3 grid(nchunk, nslice);
+    if (s_lds)
+      stats_count_kernel<true><<<grid, kStatThreads, lds, s>>>(idx, T, E, k, R, tpb, slice_rows, rank_of, S, C);
     else
-      stats_count_kernel<false, false><<<nblk, kStatThreads, lds, s>>>(idx, T, E, k, R, tpb, rank_of, S, C);
+      stats_count_kernel<false><<<grid, kStatThreads, lds, s>>>(idx, T, E, k, R, tpb, slice_rows, rank_of, S, C);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

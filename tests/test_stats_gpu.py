@@ -70,6 +70,8 @@ EDGE = [
     ("E12_k5_R3", 513, 12, 5, 3),
     ("E96_k4_R96", 800, 96, 4, 96),     # both matrices past the LDS limit
     ("E1024_k16_R1024", 300, 1024, 16, 1024),
+    ("E91_k3_R7", 700, 91, 3, 7),       # C in two row slices (90 rows + 1)
+    ("E1020_k8_R60", 400, 1020, 8, 60), # 128 slices of 8 rows, the last 4 rows
     ("T1", 1, 64, 2, 32),
 ]
 
@@ -85,6 +87,14 @@ def test_stats_more_ranks_than_experts():
     E, R = 64, 128
     rep = (np.arange(E, dtype=np.int32) * 2).reshape(E, 1)
     run_stats(synth.Workload("E64_k2_R128", 999, E, 2, 8, R, synth.BF16, "none", False), 3, rep=rep)
+
+
+def test_stats_slices_bounded_by_lds():
+    """E = 1024 on 89 ranks (expert e on rank e mod 89): S (7921 ints) stays
+    in LDS, which leaves C slices of 7 rows (146 of them, then 2 rows)."""
+    E, R = 1024, 89
+    rep = (np.arange(E, dtype=np.int32) % R).reshape(E, 1)
+    run_stats(synth.Workload("E1024_k6_R89", 600, E, 6, 8, R, synth.BF16, "none", False), 4, rep=rep)
 
 
 def test_stats_without_coselect_and_id_order():
