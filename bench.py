@@ -443,6 +443,9 @@ def main():
         "raw_rows": w.T * w.k,
         "max_active_experts": int(b.active.max().item()),
         "copy_reference_GBps": round(copy_gbps, 1),
+        "inputs": {"numpy": np.__version__,
+                   "logits_sha256": hashlib.sha256(logits.tobytes()).hexdigest()[:16],
+                   "x_sha256": hashlib.sha256(x.tobytes()).hexdigest()[:16]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": traffic},
