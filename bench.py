@@ -401,7 +401,8 @@ def main():
     achieved = half / (dom_ms / 1e3) / 1e9
     traffic = traffic_from_profiles(dom, w.name)
 
-    # a plain device copy of the dispatch's byte count, as the achievable-bandwidth reference
+    # a plain device copy of the dispatch's byte count (torch copy_, the
+    # runtime's device-to-device copy), as an achievable-bandwidth reference
     cp_src = torch.empty(half // 4, dtype=torch.int16, device=dev)
     cp_dst = torch.empty_like(cp_src)
     cp_ms = []
@@ -416,6 +417,19 @@ def main():
             cp_ms.append((a, c))
     torch.cuda.synchronize()
     copy_gbps = 2 * cp_src.numel() * 2 / (np.mean([a.elapsed_time(c) for a, c in cp_ms]) / 1e3) / 1e9
+    # a write-only reference: torch's fill of the 1 GiB flush buffer
+    fill_gbps = None
+    if flush is not None:
+        fl_ms = []
+        for i in range(6):
+            a, c = ev(), ev()
+            a.record()
+            flush.fill_(float(i))
+            c.record()
+            if i > 0:
+                fl_ms.append((a, c))
+        torch.cuda.synchronize()
+        fill_gbps = FLUSH_BYTES / (np.mean([a.elapsed_time(c) for a, c in fl_ms]) / 1e3) / 1e9
 
     res = {
         "metric": METRIC,
@@ -443,6 +457,7 @@ def main():
         "raw_rows": w.T * w.k,
         "max_active_experts": int(b.active.max().item()),
         "copy_reference_GBps": round(copy_gbps, 1),
+        "fill_reference_GBps": None if fill_gbps is None else round(fill_gbps, 1),
         "inputs": {"numpy": np.__version__,
                    "logits_sha256": hashlib.sha256(logits.tobytes()).hexdigest()[:16],
                    "x_sha256": hashlib.sha256(x.tobytes()).hexdigest()[:16]},
