@@ -121,6 +121,67 @@ def cpu_baseline(w, seed: int, tokens: int, min_seconds: float):
             "routed_rows_per_s": round(reps * sub.T * sub.k / secs, 1)}
 
 
+def cpu_next_rows(w, seed: int, tokens: int, min_seconds: float):
+    """The oracle, as it stands, on the rows beyond dispatch+combine, on the
+    same token sample as the dispatch+combine baseline, each step repeated
+    until `min_seconds` of host time (at least once), in the units of the GPU
+    legs: the single-send layout in ms, the single-send dispatch and fan-out
+    and the two backward kernels in GB/s of algorithmic bytes, the routing
+    statistics in pairs per second; the token-balanced split on the
+    replicated decode workload, as on the GPU, in pairs per second."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    def timed(fn):
+        secs, n, out = 0.0, 0, None
+        while n == 0 or secs < min_seconds:
+            t0 = time.perf_counter()
+            out = fn()
+            secs += time.perf_counter() - t0
+            n += 1
+        return secs / n, out
+
+    sub = synth.scaled(w, T=min(tokens, w.T))
+    T, k, act, rb = sub.T, sub.k, sub.act_dtype, sub.H * 2
+    x = synth.make_x(w, seed)[:T]
+    m = oracle.route_and_layout(T, sub.E, k, sub.R, synth.make_logits(w, seed)[:T],
+                                synth.replica_table(w))
+    lay_s, (ss_off, ss_row, ss_tok) = timed(
+        lambda: oracle.single_send_layout(m["idx"], m["rank_of"], sub.R))
+    n_ss = int(ss_off[-1])
+    dsp_s, send_ss = timed(lambda: oracle.single_send_dispatch(x, ss_tok))
+    exp_s, _ = timed(lambda: oracle.single_send_expand(send_ss, ss_row, m["src"]))
+    del send_ss
+    y = oracle.expert_standin(oracle.dispatch(x, m["pos"], k), m["idx"].ravel()[m["src"]], sub.E, act)
+    dout = synth.make_grad(w, seed, T)
+
+    def combine_backward():
+        dy = oracle.combine_backward_dy(dout, m["src"], m["w"], k, act)
+        oracle.combine_backward_dw(y, dout, m["pos"], k, act)
+        return dy
+
+    cb_s, dy = timed(combine_backward)
+    db_s, _ = timed(lambda: oracle.dispatch_backward(dy, m["pos"], k, act))
+    del y, dy
+    st_s, _ = timed(lambda: oracle.routing_stats(m["idx"], m["counts"], m["rank_of"], sub.E, sub.R))
+    d = synth.DECODE
+    drep = synth.replica_table(d)
+    md = oracle.route_and_layout(d.T, d.E, d.k, d.R, synth.make_logits(d, seed), drep)
+    sp_s, _ = timed(lambda: oracle.token_balanced_split(md["idx"], md["counts"], md["pos"],
+                                                        md["expert_offsets"], d.R, drep))
+    gbps = lambda nbytes, secs: round(nbytes / secs / 1e9, 3)
+    return {"sample": f"first {T} of {w.T} tokens of {w.name}; the split on {d.name}",
+            "single_send": {"layout_ms": round(lay_s * 1e3, 3),
+                            "dispatch_GBps": gbps((T + n_ss) * rb, dsp_s),
+                            "expand_GBps": gbps((n_ss + T * k) * rb, exp_s)},
+            "backward": {"combine_backward_GBps": gbps((1 + 2 * k) * T * rb, cb_s),
+                         "dispatch_backward_GBps": gbps((1 + k) * T * rb, db_s)},
+            "routing_stats_pairs_per_s": round(T * k / st_s, 1),
+            "token_balanced_split_pairs_per_s": round(d.T * d.k / sp_s, 1)}
+
+
 def warm_leg(P, b, steps, ev, np, torch, dc_bytes):
     """Dispatch and combine back to back without the cache flush: the inputs
     may then come partly from the 256 MB Infinity Cache, so this is reported
@@ -252,7 +313,8 @@ def stats_leg(P, w, b, steps, ev, np, torch):
     top = int(np.ceil(0.008 * pairs.shape[0]))
     cover = float(pairs[:top].sum()) / max(1, int(pairs.sum()))
     f = lambda v: None if not np.isfinite(v) else round(float(v), 6)
-    return {"steps": steps, "ms": round(ms, 4), "max_over_mean": f(vals[0]), "gini": f(vals[1]),
+    return {"steps": steps, "ms": round(ms, 4), "pairs_per_s": round(w.T * w.k / (ms / 1e3), 1),
+            "max_over_mean": f(vals[0]), "gini": f(vals[1]),
             "dirichlet_alpha": f(vals[2]), "locality": f(vals[3]),
             "top_0.8pct_pairs_share": round(cover, 4)}
 
@@ -286,8 +348,9 @@ def eplb_leg(P, B, synth, np, torch, dev, steps, ev, seed):
     e_act = int(sp.active.max().item())
     g_tok = int((b.rank_offsets[1:] - b.rank_offsets[:-1]).max().item())
     e_tok = int(sp.tokens.max().item())
-    return {"workload": w.name, "steps": steps,
-            "ms": round(float(np.mean([a.elapsed_time(c) for a, c in marks])), 4),
+    ms = float(np.mean([a.elapsed_time(c) for a, c in marks]))
+    return {"workload": w.name, "steps": steps, "ms": round(ms, 4),
+            "pairs_per_s": round(w.T * w.k / (ms / 1e3), 1),
             "max_activated": {"greedy": g_act, "token_balanced": e_act},
             "greedy_below_token_balanced": round(1 - g_act / e_act, 4) if e_act else None,
             "max_pairs_per_gpu": {"greedy": g_tok, "token_balanced": e_tok}}
@@ -480,6 +543,8 @@ def main():
         res["decode_graph"] = graph_leg(P, B, synth, np, torch, dev, args.graph_steps, args.seed)
     if args.cpu_tokens > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_tokens, args.cpu_seconds)
+        res["cpu_baseline"]["next_rows"] = cpu_next_rows(w, args.seed, args.cpu_tokens,
+                                                         args.cpu_seconds / 4)
     print(json.dumps(res), flush=True)
 
 
