@@ -21,6 +21,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F16, MOE_BF16 = 1, 2
 MOE_FLAG_GREEDY_ID_ORDER = 1 << 0
 MOE_FLAG_OUT_F32 = 1 << 1
+MOE_MAX_E, MOE_MAX_K, MOE_MAX_R, MOE_MAX_REP = 1024, 16, 1024, 16
+MOE_MAX_ROWS = (1 << 24) - 1
 
 EXPORTED = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
             "moe_route", "moe_assign_replicas", "moe_layout", "moe_layout_single_send",

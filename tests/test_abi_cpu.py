@@ -164,3 +164,11 @@ def test_plain_c_caller_builds_and_exports_its_check():
     from conftest import C_CHECK_LIB
     lib = ctypes.CDLL(C_CHECK_LIB)
     assert hasattr(lib, "moe_c_abi_check")
+
+
+def test_binding_limits_match_header():
+    text = open(HEADER).read()
+    for name in ("MOE_MAX_E", "MOE_MAX_K", "MOE_MAX_R", "MOE_MAX_REP"):
+        m = re.search(rf"{name} = (\d+)", text)
+        assert m and int(m.group(1)) == getattr(B, name), name
+    assert "MOE_MAX_ROWS = (1 << 24) - 1" in text and B.MOE_MAX_ROWS == (1 << 24) - 1

@@ -42,3 +42,63 @@ def test_full_size(w):
     check_rows(b, ref, x, w, sample(rng, w.T * w.k, 512), sample(rng, w.T, 256), out_f32=False)
     dispatch_identity_all_rows(b, w.k)
     assert int(b.counts.sum()) == w.T * w.k
+
+
+def test_max_rows():
+    """T*k at the row limit, 2^24 - 16 rows (T = 2^20 - 1, k = 16), with
+    64-chunk rows: the stand-in launches one 256-thread block per send row,
+    4,294,963,200 work-items, just under the 2^32 a launch holds. At this
+    size the oracle computes the sampled tokens one by one (top-k, gate
+    weights, stand-in rows, combine) from the logits and activations; the
+    index outputs are checked whole against properties that fix them: counts
+    and dedup by their definitions, pos a permutation with src its inverse
+    whose (rank, expert, token) keys strictly increase, offsets the
+    exclusive sums of the counts in that order; and the dispatch identity
+    on every row."""
+    from combine_router_topk_amd import binding as B
+    T, k, E, R, H = (1 << 20) - 1, 16, 64, 32, 512
+    assert T * k <= B.MOE_MAX_ROWS
+    w = synth.Workload("max_rows_T1048575_E64_k16_H512", T, E, k, H, R, synth.BF16, "zipf1.2", False)
+    say(f"[case] {w.name}: {T * k} rows")
+    logits = synth.make_logits(w, 0)
+    x = synth.make_x(w, 0)
+    b = run_gpu(w, logits, x, None)
+    idx = b.idx.cpu().numpy().reshape(T, k)
+    rng = np.random.default_rng(99)
+    toks = sample(rng, T, 512)
+    ref_idx = oracle.topk_select(logits[toks], k)
+    assert np.array_equal(idx[toks], ref_idx), "idx on sampled tokens"
+    ref_w = oracle.gate_weights(logits[toks], ref_idx).astype(np.float64)
+    got_w = b.w.cpu().numpy().reshape(T, k)[toks].astype(np.float64)
+    assert (np.abs(got_w - ref_w) <= 1e-6 * np.abs(ref_w)).all(), "w on sampled tokens"
+    counts = b.counts.cpu().numpy()
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E)), "counts"
+    rank_of = b.rank_of.cpu().numpy()
+    assert np.array_equal(rank_of, np.arange(E) // (E // R)), "rank_of"
+    pos, src = b.pos.cpu().numpy().astype(np.int64), b.src.cpu().numpy().astype(np.int64)
+    n = T * k
+    assert np.array_equal(np.sort(pos), np.arange(n)), "pos is a permutation"
+    assert np.array_equal(src[pos], np.arange(n)), "src inverts pos"
+    e_r = idx.ravel()[src]
+    key = (rank_of[e_r].astype(np.int64) * E + e_r) * T + src // k
+    assert (np.diff(key) > 0).all(), "rows ordered by (rank, expert, token)"
+    order = np.lexsort((np.arange(E), rank_of))
+    starts = np.zeros(E, np.int64)
+    starts[order] = np.concatenate([[0], np.cumsum(counts[order])[:-1]])
+    assert np.array_equal(b.expert_offsets.cpu().numpy(), starts), "expert_offsets"
+    roff = b.rank_offsets.cpu().numpy()
+    assert np.array_equal(roff, np.concatenate([[0], np.cumsum(np.bincount(rank_of, counts, R))]).astype(roff.dtype)), "rank_offsets"
+    ranks = rank_of[idx]
+    dedup = np.bincount(np.concatenate([np.unique(ranks[t0:t0 + 4096] + R * np.arange(t0, min(T, t0 + 4096))[:, None])
+                                        for t0 in range(0, T, 4096)]) % R, minlength=R)
+    assert np.array_equal(b.dedup.cpu().numpy(), dedup), "dedup"
+    dispatch_identity_all_rows(b, k)
+    # stand-in rows and combine outputs of the sampled tokens, from scratch
+    xs = x[toks]
+    yref = oracle.expert_standin(np.repeat(xs, k, axis=0), ref_idx.ravel(), E, w.act_dtype)
+    rows_t = torch.from_numpy(pos.reshape(T, k)[toks].ravel()).to(b.y.device)
+    got_y = b.y.index_select(0, rows_t).cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got_y, yref), "stand-in rows of sampled tokens"
+    out_ref = oracle.combine(yref, np.arange(toks.shape[0] * k), ref_w.astype(np.float32), k, w.act_dtype)
+    got = b.out.index_select(0, torch.from_numpy(toks).to(b.out.device)).float().cpu().numpy().astype(np.float64)
+    assert (np.abs(got - out_ref) <= 1e-3 + 4e-3 * np.abs(out_ref)).all(), "combine of sampled tokens"
