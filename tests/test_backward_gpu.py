@@ -168,6 +168,17 @@ def test_backward_edge_shapes(name, T, E, k, R, H):
     run_backward(synth.Workload(name, T, E, k, H, R, synth.BF16, "none", False), 5)
 
 
+# Row widths past the one-chunk shape (16-byte chunks per row: 257, 375,
+# 513, 1024, 1537), k up to 8 (two chunk positions per step).
+WIDTHS = [("H2056_k3", 2056, 3), ("H3000_k8", 3000, 8), ("H4104_k4", 4104, 4),
+          ("H8192_k6", 8192, 6), ("H12296_k7", 12296, 7)]
+
+
+@pytest.mark.parametrize("name,H,k", WIDTHS, ids=[v[0] for v in WIDTHS])
+def test_backward_row_widths(name, H, k):
+    run_backward(synth.Workload(name, 300, 16, k, H, 4, synth.BF16, "zipf1.2", False), 6)
+
+
 def test_backward_empty_batch_and_errors():
     w = synth.Workload("bwd_empty", 0, 8, 2, 128, 4, synth.F16, "none", False)
     say("[case] backward empty batch and argument errors")

@@ -89,6 +89,20 @@ EDGE = [
 ]
 
 
+# Row widths at every launch-shape boundary of the row kernels (16-byte
+# chunks per row): 257 and 375 (two chunks per lane, the second ragged),
+# 513, 768 and 1024 (the 128-thread dispatch with 5, 6 and 8 chunks per
+# lane), 1537 (rows past 1024 chunks: the dispatch loops); k from 3 to 8
+# covers the combine's compile-time-k instances.
+WIDTHS = [("H2056_k3", 2056, 3), ("H3000_k5", 3000, 5), ("H4104_k4", 4104, 4),
+          ("H6144_k6", 6144, 6), ("H8192_k8", 8192, 8), ("H12296_k7", 12296, 7)]
+
+
+@pytest.mark.parametrize("name,H,k", WIDTHS, ids=[v[0] for v in WIDTHS])
+def test_row_widths(name, H, k):
+    run_and_check(synth.Workload(name, 300, 16, k, H, 4, synth.BF16, "zipf1.2", False), 6)
+
+
 @pytest.mark.parametrize("name,T,E,k,R,H", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_shapes(name, T, E, k, R, H):
     w = synth.Workload(name, T, E, k, H, R, synth.BF16, "none", False)

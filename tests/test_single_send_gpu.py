@@ -124,6 +124,22 @@ def test_single_send_edge_shapes(name, T, E, k, R, H):
     check_single_send(w, b, ss, ex, ref)
 
 
+# Row widths (16-byte chunks per row: 257, 375, 513, 1024, 1537): the
+# dispatch's long-row shapes and the fan-out's two chunks per lane.
+WIDTHS = [("H2056_k3", 2056, 3), ("H3000_k5", 3000, 5), ("H4104_k4", 4104, 4),
+          ("H8192_k8", 8192, 8), ("H12296_k7", 12296, 7)]
+
+
+@pytest.mark.parametrize("name,H,k", WIDTHS, ids=[v[0] for v in WIDTHS])
+def test_single_send_row_widths(name, H, k):
+    w = synth.Workload(name, 300, 16, k, H, 4, synth.BF16, "zipf1.2", False)
+    say(f"[case] single-send row width {name}")
+    logits, x = synth.make_logits(w, 6), synth.make_x(w, 6)
+    ref = oracle.route_and_layout(w.T, w.E, w.k, w.R, logits)
+    b, ss, ex = run_single_send(w, logits, x, None)
+    check_single_send(w, b, ss, ex, ref)
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_single_send_random_replicas_id_order(seed):
     rng = np.random.default_rng(300 + seed)
