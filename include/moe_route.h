@@ -9,11 +9,11 @@
  * routing as the greedy's baseline.
  *
  * Sources (web pages on MoE dispatch and combine):
- *   [METRO]  "METRO AllGather vs AllToAll for MoE decode" (fanout.sh).
+ *   [METRO]  "METRO AllGather vs AllToAll for MoE decode".
  *   [CORR]   News summary of "correlated expert placement and token
- *            shuffling" for MoE pretraining (ainewsletter.today).
+ *            shuffling" for MoE pretraining.
  *   [DODOCO] "Diagnosing Overhead in Dispatch Operations: Cross-architecture
- *            Observatory" (gist.science).
+ *            Observatory".
  *
  * Conventions shared by every call
  * --------------------------------
