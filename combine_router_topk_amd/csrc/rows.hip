@@ -294,19 +294,31 @@ int threads_per_row(int cpr) {
 // every one-row kernel over H = 2048, 4096, 7168 and k = 2..8 (reservations
 // 0 to 64 KiB); each rule names the measured gain over no reservation.
 
-// Dispatch (plain and single-send): rows over 512 chunks use 128-thread
-// blocks, best with 24 KiB at k <= 2 and 32 KiB above (H = 7168: 5-8%);
-// 257-512 chunks with k >= 4: 64 KiB (H = 4096, k = 4: 9%); otherwise 48 KiB
-// (H = 4096, k = 2: 71 vs 81 us; H = 2048, k = 6: 86 vs 93 us).
+// Dispatch (plain and single-send), per launch shape (see launch_dispatch):
+//  - rows over 512 chunks, 128-thread blocks: 24 KiB at k <= 2, 32 KiB above
+//    (H = 7168: 5-8%);
+//  - 257-512 chunks, 256-thread blocks: 64 KiB at k >= 4 (H = 4096, k = 4:
+//    9%), else 48 KiB (H = 4096, k = 2: 71 vs 81 us);
+//  - 129-256 chunks, 128-thread blocks: 24 KiB (measured with the shape);
+//  - at most 128 chunks, several rows per 256-thread block: 48 KiB.
 size_t dispatch_reserve(int k, int cpr) {
   if (cpr > 512) return (k <= 2 ? 24 : 32) * kKiB;
-  if (cpr > 256 && k >= 4) return 64 * kKiB;
+  if (cpr > 256) return (k >= 4 ? 64 : 48) * kKiB;
+  if (cpr > 128) return 24 * kKiB;
   return 48 * kKiB;
 }
 
-// Blocks of a dispatch launch: one row each, or several rows under 64 chunks.
+// The dispatch gives a block several rows whenever a row needs fewer than
+// kRowThreads lanes (rows of at most 128 chunks), so no lane idles while the
+// LDS reservation caps the blocks per CU: at H = 512, k = 8 one row per
+// block took 116 us and four rows 62 us; at H = 1024, k = 2, 77 against
+// 45 us. Rows of 129 to 256 chunks keep one row per block (the several-row
+// kernel with one row was 7% slower there).
+bool dispatch_multi_row(int cpr) { return threads_per_row(cpr) < kRowThreads; }
+
+// Blocks of a dispatch launch.
 long long dispatch_blocks(int T, int cpr) {
-  if (cpr >= kOneRowChunks) return T;
+  if (!dispatch_multi_row(cpr)) return T;
   const int per_blk = kRowThreads / threads_per_row(cpr);
   return (T + per_blk - 1) / per_blk;
 }
@@ -372,13 +384,18 @@ hipError_t launch_combine_a(const u32x4* y, const int32_t* pos, const float* w, 
 
 }  // namespace
 
-// Launch shape of the dispatch, from measurements on MI355X (cold cache):
-//  - rows of at most 512 chunks (H <= 4096): 256-thread blocks, one row per
-//    block (several for rows under 64 chunks);
+// Launch shape of the dispatch, from measurements on MI355X (cold cache),
+// each with the LDS reservation of dispatch_reserve:
+//  - rows of at most 128 chunks: several rows per 256-thread block (see
+//    dispatch_multi_row);
+//  - 129-256 chunks: 128-thread blocks, two chunks per lane, one row per
+//    block. Against 256-thread blocks with one chunk per lane (48 KiB):
+//    H = 2048, k = 2: 70 vs 90 us; H = 1536, k = 2: 56 vs 85 us; H = 1280,
+//    k = 4: 77 vs 98 us; H = 2048, k = 6: 86 us either way;
+//  - 257-512 chunks: 256-thread blocks, two chunks per lane;
 //  - longer rows (H = 7168): 128-thread blocks with ceil(cpr / 128) chunks
 //    per lane and serialized row loads (1.63 ms against 1.69-1.77 ms for
-//    256-thread shapes at full occupancy);
-//  - the LDS reservation of dispatch_reserve in both cases.
+//    256-thread shapes at full occupancy).
 
 hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T, int k, int H,
                            hipStream_t s) {
@@ -387,13 +404,13 @@ hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T,
   const u32x4* xv = static_cast<const u32x4*>(x);
   u32x4* sv = static_cast<u32x4*>(send);
   const size_t res = if_many_blocks(dispatch_reserve(k, cpr), dispatch_blocks(T, cpr));
-  if (cpr < kOneRowChunks) {
+  if (dispatch_multi_row(cpr)) {
     const int tpt = threads_per_row(cpr);
     const int per_blk = kRowThreads / tpt;
     dispatch_kernel<kRowThreads, 1, false><<<(T + per_blk - 1) / per_blk, kRowThreads, res, s>>>(
         xv, pos, sv, T, k, cpr, tpt);
   } else if (cpr <= 256) {
-    dispatch_kernel<kRowThreads, 1, true><<<T, kRowThreads, res, s>>>(xv, pos, sv, T, k, cpr, 0);
+    dispatch_kernel<128, 2, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
   } else if (cpr <= 512) {
     dispatch_kernel<kRowThreads, 2, true><<<T, kRowThreads, res, s>>>(xv, pos, sv, T, k, cpr, 0);
   } else {
@@ -415,13 +432,13 @@ hipError_t launch_single_send_dispatch(const void* x, const int32_t* ss_row, voi
   u32x4* sv = static_cast<u32x4*>(send_ss);
   const size_t res = if_many_blocks(dispatch_reserve(k, cpr), dispatch_blocks(T, cpr));
   const int cap = ss_capacity;
-  if (cpr < kOneRowChunks) {
+  if (dispatch_multi_row(cpr)) {
     const int tpt = threads_per_row(cpr);
     const int per_blk = kRowThreads / tpt;
     dispatch_kernel<kRowThreads, 1, false, false, true><<<(T + per_blk - 1) / per_blk, kRowThreads, res, s>>>(
         xv, ss_row, sv, T, k, cpr, tpt, cap);
   } else if (cpr <= 256) {
-    dispatch_kernel<kRowThreads, 1, true, false, true><<<T, kRowThreads, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
+    dispatch_kernel<128, 2, true, false, true><<<T, 128, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
   } else if (cpr <= 512) {
     dispatch_kernel<kRowThreads, 2, true, false, true><<<T, kRowThreads, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
   } else {
