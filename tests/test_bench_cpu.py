@@ -1,0 +1,35 @@
+"""The benchmark's host-side parts without a GPU: it refuses more than one
+GPU before touching the device, and its oracle baselines (dispatch+combine,
+and the rows beyond it) run on a small sample and report the fields the
+JSON line carries."""
+import os
+import subprocess
+import sys
+
+import synth
+from conftest import ROOT
+
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_cpu_baseline_fields():
+    w = synth.scaled(synth.TRAIN_TOP2, T=64, H=64)
+    c = bench.cpu_baseline(w, 0, 64, 0.0)
+    assert set(c) >= {"value", "unit", "cores", "kind", "sample"}
+    assert c["unit"] == "GB/s" and c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0
+
+
+def test_cpu_next_rows_fields():
+    w = synth.scaled(synth.TRAIN_TOP2, T=64, H=64)
+    n = bench.cpu_next_rows(w, 0, 64, 0.0)
+    assert n["single_send"]["dispatch_GBps"] > 0 and n["single_send"]["expand_GBps"] > 0
+    assert n["backward"]["combine_backward_GBps"] > 0 and n["backward"]["dispatch_backward_GBps"] > 0
+    assert n["routing_stats_pairs_per_s"] > 0 and n["token_balanced_split_pairs_per_s"] > 0
