@@ -115,7 +115,14 @@ def cpu_baseline(w, seed: int, tokens: int, min_seconds: float):
         reps += 1
         del send, y
     nbytes = sub.dispatch_combine_bytes() * reps
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(nbytes / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "host_cpu": cpu_model, "host_threads": os.cpu_count(),
             "sample": f"first {sub.T} of {w.T} tokens of {w.name}, {reps} passes; oracle dispatch + "
                       f"fp64 combine ({secs:.2f} s for {nbytes} algorithmic bytes)",
             "routed_rows_per_s": round(reps * sub.T * sub.k / secs, 1)}
