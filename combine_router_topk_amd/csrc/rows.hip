@@ -11,8 +11,9 @@
 // target" (each layer dispatches tokens and combines results).
 //
 // All are HBM-bound streams of 16-byte chunks. A row is split over a
-// team of TPT lanes (TPT a power of two, up to the 256-thread block); small
-// rows pack several tokens into one block. Each lane issues all of its loads
+// team of lanes (a power of two, up to the block: 256 threads, or 128 for
+// the dispatch's 129-256-chunk and longest rows); small rows pack several
+// tokens into one block. Each lane issues all of its loads
 // before its stores or arithmetic so many 16-byte requests are in flight.
 // Dispatch reads each token row once and writes its k copies (the minimum
 // traffic); combine reads the k rows of a token and writes one.
@@ -33,8 +34,9 @@ __device__ __forceinline__ u32x4 to_vec(uint4 v) { return u32x4{v.x, v.y, v.z, v
 
 // Row teams. With ONE = true a block is one row: the row index is uniform,
 // so the row's pos / w / src entries come through scalar loads and the lane
-// stride is the compile-time block size. With ONE = false (rows shorter than
-// 64 chunks) a block holds NT / tpt rows of tpt lanes each.
+// stride is the compile-time block size. With ONE = false (short rows: under
+// 64 chunks, or up to 128 chunks for the dispatch) a block holds NT / tpt
+// rows of tpt lanes each.
 template <int NT, bool ONE>
 __device__ __forceinline__ void row_team(int tpt, int& row, int& lane, int& stride) {
   if constexpr (ONE) {
@@ -275,7 +277,8 @@ __global__ __launch_bounds__(NT) void fanout_kernel(
   }
 }
 
-// Rows of at least this many 16-byte chunks get a block each.
+// Rows of at least this many 16-byte chunks get a block each (the dispatch
+// decides by dispatch_multi_row instead).
 constexpr int kOneRowChunks = 64;
 
 // Threads per row for short rows: enough for one 16-byte chunk each.
