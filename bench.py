@@ -4,7 +4,8 @@ One step = one pass of the whole path over one batch resident in HBM:
 route (top-k, gate weights, demand vector) -> greedy replica assignment ->
 layout (offsets, permutation, dedup) -> dispatch -> expert stand-in ->
 combine. The headline is dispatch+combine GB/s of algorithmic bytes,
-2 (1 + k) T H b, over the two kernels' HIP-event durations, and routed rows/s
+2 (1 + k) T H b, over the two kernels' HIP-event durations (events without
+the system-scope fence, see timing_event_type), and routed rows/s
 (T k rows over the same time). By default the 256 MB Infinity Cache and the L2s
 are flushed (a 1 GiB fill) before the dispatch and before the combine, outside
 their event brackets, so both read from HBM.
@@ -85,6 +86,48 @@ def traffic_from_profiles(kernel: str, workload: str):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def timing_event_type(lib, torch):
+    """HIP timing events with the interface of torch.cuda.Event(enable_timing=
+    True), taken from the HIP runtime the routing library launches with (its
+    handle resolves the runtime's symbols) and recorded on torch's current
+    stream, which is the stream the library's kernels run on. They are created
+    with hipEventDisableSystemFence: recording one then skips the system-scope
+    cache writeback and invalidation, which the HIP headers name as the more
+    accurate choice for events used only to time work. Elapsed times are read
+    after a device synchronisation."""
+    import ctypes
+    vp = ctypes.c_void_p
+    create, record = lib.hipEventCreateWithFlags, lib.hipEventRecord
+    elapsed, destroy = lib.hipEventElapsedTime, lib.hipEventDestroy
+    create.argtypes, create.restype = [ctypes.POINTER(vp), ctypes.c_uint], ctypes.c_int
+    record.argtypes, record.restype = [vp, vp], ctypes.c_int
+    elapsed.argtypes, elapsed.restype = [ctypes.POINTER(ctypes.c_float), vp, vp], ctypes.c_int
+    destroy.argtypes, destroy.restype = [vp], ctypes.c_int
+    disable_system_fence = 0x20000000
+
+    class Event:
+        def __init__(self):
+            self.h = vp()
+            if create(ctypes.byref(self.h), disable_system_fence) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+
+        def record(self):
+            if record(self.h, vp(torch.cuda.current_stream().cuda_stream)) != 0:
+                raise RuntimeError("hipEventRecord failed")
+
+        def elapsed_time(self, end) -> float:
+            ms = ctypes.c_float()
+            if elapsed(ctypes.byref(ms), self.h, end.h) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            return ms.value
+
+        def __del__(self):
+            if self.h:
+                destroy(self.h)
+
+    return Event
 
 
 def cpu_baseline(w, seed: int, tokens: int, min_seconds: float):
@@ -420,7 +463,7 @@ def main():
     flush = None if args.warm_cache else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ev = timing_event_type(B._lib, torch)
     marks, meta_marks = [], []
 
     def step(record: bool):

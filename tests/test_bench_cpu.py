@@ -33,3 +33,12 @@ def test_cpu_next_rows_fields():
     assert n["single_send"]["dispatch_GBps"] > 0 and n["single_send"]["expand_GBps"] > 0
     assert n["backward"]["combine_backward_GBps"] > 0 and n["backward"]["dispatch_backward_GBps"] > 0
     assert n["routing_stats_pairs_per_s"] > 0 and n["token_balanced_split_pairs_per_s"] > 0
+
+
+def test_timing_events_resolve_through_the_library():
+    """The bench's timing events come from the HIP runtime the routing
+    library is linked against (no event is created without a GPU)."""
+    import torch
+    from combine_router_topk_amd import binding as B
+    Ev = bench.timing_event_type(B._lib, torch)
+    assert callable(Ev) and {"record", "elapsed_time"} <= set(dir(Ev))
