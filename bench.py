@@ -399,7 +399,10 @@ def eplb_leg(P, B, synth, np, torch, dev, steps, ev, seed):
     g_tok = int((b.rank_offsets[1:] - b.rank_offsets[:-1]).max().item())
     e_tok = int(sp.tokens.max().item())
     ms = float(np.mean([a.elapsed_time(c) for a, c in marks]))
+    rec = P.record(b)
     return {"workload": w.name, "steps": steps, "ms": round(ms, 4),
+            "routing_record": {key: rec[key] for key in ("send_bytes", "dedup_rows", "active_per_gpu",
+                                                        "assign")},
             "pairs_per_s": round(w.T * w.k / (ms / 1e3), 1),
             "max_activated": {"greedy": g_act, "token_balanced": e_act},
             "greedy_below_token_balanced": round(1 - g_act / e_act, 4) if e_act else None,

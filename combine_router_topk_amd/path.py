@@ -115,6 +115,36 @@ def capture(b: Buffers, steps=STEPS) -> torch.cuda.CUDAGraph:
     return g
 
 
+def record(b: Buffers, ss: SingleSend | None = None) -> dict:
+    """Host-side record of one routed batch: what "METRO AllGather vs AllToAll
+    for MoE decode", section "Distinguish METRO from backend names", asks to
+    keep beside collective traces (buffer sizes per destination rank and the
+    expert replica chosen for each expert's global count), plus the dedup
+    total and the activated experts per GPU. Reads back 2E + 3R + 1 ints of
+    metadata (R + 1 more with `ss`; this synchronises the stream), never the
+    rows.
+
+    send_bytes[r] is rank r's segment of the send buffer, the size of the
+    all-to-all chunk for destination r; with `ss`, ss_send_bytes[r] is the
+    same for the single-send buffer."""
+    p = b.p
+    row_bytes = p.H * 2  # 16-bit activations
+    roff = b.rank_offsets.cpu().tolist()
+    rec = {
+        "T": p.T, "E": p.E, "k": p.k, "H": p.H, "R": p.R,
+        "send_bytes": [(roff[r + 1] - roff[r]) * row_bytes for r in range(p.R)],
+        "rows": roff[-1],
+        "dedup_rows": int(b.dedup.sum().item()),
+        "active_per_gpu": b.active.cpu().tolist(),
+        "counts": b.counts.cpu().tolist(),
+        "assign": b.assign.cpu().tolist(),
+    }
+    if ss is not None:
+        so = ss.ss_rank_offsets.cpu().tolist()
+        rec["ss_send_bytes"] = [(so[r + 1] - so[r]) * row_bytes for r in range(p.R)]
+    return rec
+
+
 @dataclass
 class SingleSend:
     """Single-send buffers: one row per (token, destination rank). The row

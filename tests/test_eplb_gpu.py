@@ -3,6 +3,8 @@ through the C ABI, on the route and layout the GPU wrote (checked against the
 oracle first): the GPU of every pair, the activated replicas and the pairs
 served per GPU, all bit-exact; plus the decode-table closed form (36 activated
 experts per GPU under token balance, 32 under the greedy)."""
+import json
+
 import numpy as np
 import pytest
 import torch
@@ -104,3 +106,26 @@ def test_split_edge_shapes_and_empty():
     P.token_balanced_split(b, sp)
     torch.cuda.synchronize()
     assert host(sp.active).tolist() == [0] * 4 and host(sp.tokens).tolist() == [0] * 4
+
+
+def test_routing_record_matches_the_oracle():
+    """path.record on the replicated decode workload: per-rank send bytes,
+    the dedup total, activated experts per GPU and the assign map, against
+    the oracle; the single-send bytes sum to the dedup rows."""
+    w = synth.DECODE
+    say("[case] routing record")
+    logits, x = synth.make_logits(w, 1), synth.make_x(w, 1)
+    rep = synth.replica_table(w)
+    ref = oracle.route_and_layout(w.T, w.E, w.k, w.R, logits, rep)
+    b = run_gpu(w, logits, x, rep)
+    ss = P.allocate_single_send(b)
+    P.layout_single_send(b, ss)
+    rec = P.record(b, ss)
+    rb = w.H * 2
+    assert rec["send_bytes"] == (np.diff(ref["rank_offsets"]) * rb).tolist()
+    assert sum(rec["send_bytes"]) == w.T * w.k * rb and rec["rows"] == w.T * w.k
+    assert rec["dedup_rows"] == int(ref["dedup"].sum())
+    assert sum(rec["ss_send_bytes"]) == rec["dedup_rows"] * rb
+    assert rec["active_per_gpu"] == ref["active"].tolist()
+    assert rec["assign"] == ref["assign"].tolist() and rec["counts"] == ref["counts"].tolist()
+    json.dumps(rec)
