@@ -109,9 +109,15 @@ def test_edge_shapes(name, T, E, k, R, H):
     run_and_check(w, 5)
 
 
-def test_ties_signed_zeros_nan_inf():
-    rng = np.random.default_rng(7)
-    T, E, k, R = 700, 16, 5, 4
+# every route kernel shape: 16 lanes x 1 (E = 16), 32 x 4 (E = 100), one
+# token per wave with 4, 8 and 16 logits per lane (E = 256, 384, 1024)
+TIES = [(16, 5, 4), (100, 7, 4), (256, 8, 8), (384, 10, 12), (1024, 16, 16)]
+
+
+@pytest.mark.parametrize("E,k,R", TIES, ids=[f"E{e}_k{k}" for e, k, _ in TIES])
+def test_ties_signed_zeros_nan_inf(E, k, R):
+    rng = np.random.default_rng(7 + E)
+    T = 700
     l = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
     l[rng.random((T, E)) < 0.2] = -0.0
     l[rng.random((T, E)) < 0.05] = np.nan
