@@ -113,6 +113,17 @@ def _ptr(t: torch.Tensor | None, dtype: torch.dtype | None, numel: int | None, n
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _nbytes(t: torch.Tensor | None) -> int:
+    """Byte size of a workspace tensor; 0 for None (the library then reports
+    the NULL pointer)."""
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _rows(t: torch.Tensor | None) -> int:
+    """Row count of a single-send buffer (its capacity); 0 for None."""
+    return 0 if t is None else t.shape[0]
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -145,7 +156,7 @@ def moe_route(p: Problem, logits, idx, w, counts, ws, stream=None) -> None:
                           _ptr(logits, torch.float32, p.T * p.E, "logits"),
                           _ptr(idx, torch.int32, n, "idx"), _ptr(w, torch.float32, n, "w"),
                           _ptr(counts, torch.int32, p.E, "counts"), _ptr(ws, None, None, "ws"),
-                          ws.numel() * ws.element_size(), _stream(stream)), "moe_route")
+                          _nbytes(ws), _stream(stream)), "moe_route")
 
 
 def moe_assign_replicas(p: Problem, counts, rep, maxrep: int, assign, active, stream=None) -> None:
@@ -167,7 +178,7 @@ def moe_layout(p: Problem, idx, assign, rep, maxrep: int, rank_of, expert_offset
                            _ptr(rank_offsets, torch.int32, p.R + 1, "rank_offsets"),
                            _ptr(pos, torch.int32, n, "pos"), _ptr(src, torch.int32, n, "src"),
                            _ptr(dedup, torch.int32, p.R, "dedup"), _ptr(ws, None, None, "ws"),
-                           ws.numel() * ws.element_size(), _stream(stream)), "moe_layout")
+                           _nbytes(ws), _stream(stream)), "moe_layout")
 
 
 def moe_layout_single_send(p: Problem, idx, assign, rep, maxrep: int, rank_of, expert_offsets,
@@ -184,14 +195,14 @@ def moe_layout_single_send(p: Problem, idx, assign, rep, maxrep: int, rank_of, e
         _ptr(dedup, torch.int32, p.R, "dedup"),
         _ptr(ss_rank_offsets, torch.int32, p.R + 1, "ss_rank_offsets"),
         _ptr(ss_row, torch.int32, n, "ss_row"), _ptr(ss_token, torch.int32, n, "ss_token"),
-        _ptr(ws, None, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+        _ptr(ws, None, None, "ws"), _nbytes(ws), _stream(stream)),
         "moe_layout_single_send")
 
 
 def moe_single_send_dispatch(p: Problem, x, ss_row, send_ss, stream=None) -> None:
     """send_ss holds the single-send rows; its row count is the capacity."""
     act = _TORCH_ACT.get(p.act_dtype)
-    cap = send_ss.shape[0] if send_ss is not None else 0
+    cap = _rows(send_ss)
     _check(_lib.moe_single_send_dispatch(ctypes.byref(p), _ptr(x, act, p.T * p.H, "x"),
                                          _ptr(ss_row, torch.int32, p.T * p.k, "ss_row"),
                                          _ptr(send_ss, act, cap * p.H, "send_ss"), cap,
@@ -203,7 +214,7 @@ def moe_single_send_expand(p: Problem, send_ss, ss_rank_offsets, ss_token, ss_ro
     """send_ss holds the single-send rows; its row count is the capacity."""
     act = _TORCH_ACT.get(p.act_dtype)
     n = p.T * p.k
-    cap = send_ss.shape[0]
+    cap = _rows(send_ss)
     _check(_lib.moe_single_send_expand(ctypes.byref(p), _ptr(send_ss, act, cap * p.H, "send_ss"),
                                        _ptr(ss_rank_offsets, torch.int32, p.R + 1, "ss_rank_offsets"),
                                        _ptr(ss_token, torch.int32, min(cap, n), "ss_token"),

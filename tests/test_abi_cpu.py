@@ -172,3 +172,19 @@ def test_binding_limits_match_header():
         m = re.search(rf"{name} = (\d+)", text)
         assert m and int(m.group(1)) == getattr(B, name), name
     assert "MOE_MAX_ROWS = (1 << 24) - 1" in text and B.MOE_MAX_ROWS == (1 << 24) - 1
+
+
+def test_binding_hands_missing_buffers_to_the_library_checks():
+    # a missing workspace or buffer reaches the library as NULL with 0 bytes,
+    # and comes back as a MoeError naming it (stream 0: nothing is enqueued)
+    p = B.make_problem(4, 8, 2, 64, 4, B.MOE_BF16)
+    with pytest.raises(B.MoeError, match="counts is NULL") as e:
+        B.moe_route(p, None, None, None, None, None, stream=0)
+    assert e.value.status == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoeError, match="is NULL"):
+        B.moe_layout(p, None, None, None, 1, *(None,) * 7, stream=0)
+    with pytest.raises(B.MoeError, match="is NULL"):
+        B.moe_layout_single_send(p, None, None, None, 1, *(None,) * 10, stream=0)
+    # a single-send buffer of no rows has capacity 0: nothing is written
+    B.moe_single_send_dispatch(p, None, None, None, stream=0)
+    B.moe_single_send_expand(p, *(None,) * 6, stream=0)
