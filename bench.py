@@ -439,6 +439,22 @@ def graph_leg(P, B, synth, np, torch, dev, steps, seed):
             "graph_us_per_step": round(graph_us, 1)}
 
 
+def path_summary(w, meta_ms: dict, disp_ms: float, comb_ms: float, dc_bytes: int) -> dict:
+    """The whole forward path (route, assign, layout, dispatch, combine; the
+    expert stand-in and the cache flushes excluded), kernel time summed per
+    stage. Algorithmic bytes: dispatch and combine rows, the logits, and 32
+    bytes of metadata per (token, slot) pair (route writes idx and w; layout
+    reads idx and writes pos and src; dispatch reads pos; combine reads pos
+    and w)."""
+    ms = sum(meta_ms.values()) + disp_ms + comb_ms
+    nbytes = dc_bytes + w.T * w.E * 4 + 32 * w.T * w.k
+    return {"us": round(ms * 1e3, 2), "bytes": nbytes,
+            "GBps": round(nbytes / (ms / 1e3) / 1e9, 2),
+            "frac_of_peak": round(nbytes / (ms / 1e3) / 1e9 / PEAK_GBPS, 4),
+            "routed_rows_per_s": round(w.T * w.k / (ms / 1e3), 1),
+            "metadata_share_of_time": round(sum(meta_ms.values()) / ms, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -565,6 +581,7 @@ def main():
                    "cache": "warm" if flush is None else "cold: 1 GiB fill before dispatch and before combine"},
         "frac_of_peak": round(value / PEAK_GBPS, 4),
         "routed_rows_per_s": round(w.T * w.k / dc_s, 1),
+        "path": path_summary(w, meta_ms, disp_ms, comb_ms, dc_bytes),
         "stage_ms": {**{k_: round(v_, 4) for k_, v_ in meta_ms.items()},
                      "dispatch": round(disp_ms, 4), "combine": round(comb_ms, 4)},
         "median_ms": {"dispatch": round(float(np.median(disp_all)), 4),

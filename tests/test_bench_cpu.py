@@ -42,3 +42,16 @@ def test_timing_events_resolve_through_the_library():
     from combine_router_topk_amd import binding as B
     Ev = bench.timing_event_type(B._lib, torch)
     assert callable(Ev) and {"record", "elapsed_time"} <= set(dir(Ev))
+
+
+def test_path_summary_arithmetic():
+    # train top-2: 768 MiB of rows + 4 MiB of logits + 32 B per pair, over
+    # 100 us of summed stage time
+    w = synth.TRAIN_TOP2
+    dc = w.dispatch_combine_bytes()
+    s = bench.path_summary(w, {"route": 0.005, "assign": 0.005, "layout": 0.01}, 0.04, 0.04, dc)
+    want = 805_306_368 + 16384 * 64 * 4 + 32 * 16384 * 2
+    assert s["bytes"] == want and s["us"] == 100.0
+    assert abs(s["GBps"] - want / 100e-6 / 1e9) < 0.01
+    assert s["metadata_share_of_time"] == 0.2
+    assert abs(s["routed_rows_per_s"] - 32768 / 100e-6) < 1
