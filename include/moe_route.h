@@ -219,7 +219,9 @@ moe_status moe_single_send_expand(const moe_problem* p, const void* send_ss,
  * [METRO] section "Work the 8-GPU payload example" (the dispatch payload is
  * token activation rows).
  *   x     16-bit [T, H] (read)    pos  i32 [T*k] (read)
- *   send  16-bit [T*k, H] (write); must not overlap x                       */
+ *   send  16-bit [T*k, H] (write); must not overlap x
+ * A slot whose pos is outside [0, T*k) is skipped: no row is written for
+ * it.                                                                      */
 moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* pos, void* send,
                         void* stream);
 
@@ -228,7 +230,8 @@ moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* pos,
  * with s = 1 + e/E, s and the product each rounded to fp32, round16 to
  * nearest-even in the activation format.
  *   send 16-bit [T*k, H] (read)  src i32 [T*k]  idx i32 [T, k]
- *   y    16-bit [T*k, H] (write); may alias send                           */
+ *   y    16-bit [T*k, H] (write); may alias send
+ * A row whose src is outside [0, T*k) is scaled as expert 0 (s = 1).      */
 moe_status moe_expert_standin(const moe_problem* p, const void* send, const int32_t* src,
                               const int32_t* idx, void* y, void* stream);
 
@@ -240,7 +243,9 @@ moe_status moe_expert_standin(const moe_problem* p, const void* send, const int3
  * information" (expert outputs return through a combine); [CORR] section
  * "Why communication is the target".
  *   y    16-bit [T*k, H] (read)  pos i32 [T*k]  w f32 [T, k]
- *   out  [T, H] in the activation format or fp32 (write); must not overlap y */
+ *   out  [T, H] in the activation format or fp32 (write); must not overlap y
+ * A slot whose pos is outside [0, T*k) takes weight 0 on row 0: it adds
+ * nothing while row 0 is finite.                                           */
 moe_status moe_combine(const moe_problem* p, const void* y, const int32_t* pos, const float* w,
                        void* out, void* stream);
 

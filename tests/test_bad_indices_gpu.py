@@ -1,0 +1,131 @@
+"""Out-of-range send positions and sources reach only the kernels' own bounds
+checks: each row kernel tests every pos and src entry against the buffer it
+addresses, so a corrupt entry is skipped rather than followed. Dispatch
+leaves the row the slot would have written untouched; combine and dispatch
+backward add nothing for it; combine backward writes no dy row and a dw of
+0; the stand-in scales a row whose source is out of range as expert 0. Every
+other output equals the oracle's on the same corrupted tables (the oracle
+reads an appended zero row for each skipped slot, which contributes nothing
+to a sum). All accesses stay inside the buffers: the corrupt values are
+never used as addresses."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from combine_router_topk_amd import binding as B
+from pathcheck import OUT_ATOL, OUT_RTOL, bits_to_tensor, host, run_gpu, say, tensor_bits
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7E5A
+BAD_VALUES = np.array([-1, -2**31, 2**31 - 1], np.int64)
+
+
+def corrupt(pos: np.ndarray, n_rows: int, rng) -> tuple[np.ndarray, np.ndarray]:
+    """About 5% of the entries replaced by out-of-range values (negative,
+    n_rows, n_rows + 7 and the int32 extremes); returns the table and the mask."""
+    bad = rng.random(pos.shape[0]) < 0.05
+    bad[0] = True  # the first token always has a corrupt slot
+    vals = np.concatenate([BAD_VALUES, [n_rows, n_rows + 7]])
+    out = pos.astype(np.int64).copy()
+    out[bad] = vals[rng.integers(len(vals), size=int(bad.sum()))]
+    return out.astype(np.int32), bad
+
+
+def with_zero_row(rows: np.ndarray) -> np.ndarray:
+    return np.concatenate([rows, np.zeros((1, rows.shape[1]), rows.dtype)])
+
+
+SHAPES = [
+    ("H264_k6", 600, 64, 6, 264, 8),     # several rows per block, combine one chunk position per step
+    ("H2056_k2", 400, 16, 2, 2056, 4),   # 128-thread blocks, two chunks per lane
+    ("H4104_k4", 300, 32, 4, 4104, 8),   # rows past 512 chunks
+]
+
+
+@pytest.mark.parametrize("name,T,E,k,H,R", SHAPES, ids=[s[0] for s in SHAPES])
+def test_out_of_range_positions_are_skipped(name, T, E, k, H, R):
+    rng = np.random.default_rng(11)
+    w = synth.Workload(name, T, E, k, H, R, synth.BF16, "zipf1.2", False)
+    logits, x = synth.make_logits(w, 3), synth.make_x(w, 3)
+    say(f"[case] out-of-range positions {name}")
+    ref = oracle.route_and_layout(T, E, k, R, logits)
+    b = run_gpu(w, logits, x, None)
+    n = T * k
+    assert np.array_equal(host(b.pos), ref["pos"]) and np.array_equal(host(b.src), ref["src"])
+    pos_bad, bad = corrupt(ref["pos"], n, rng)
+    orphan = np.zeros(n, bool)
+    orphan[ref["pos"][bad]] = True          # rows no valid slot writes
+    pos_zero = np.where(bad, n, ref["pos"])  # the oracle's appended zero row
+    p = B.make_problem(T, E, k, H, R, w.act_dtype)
+    pos_t = torch.from_numpy(pos_bad).cuda()
+    act = b.x.dtype
+
+    # dispatch: orphaned rows untouched, the rest bit copies
+    send = torch.empty_like(b.send)
+    send.view(torch.int16).fill_(SENTINEL)
+    B.moe_dispatch(p, b.x, pos_t, send)
+    torch.cuda.synchronize()
+    got = tensor_bits(send)
+    assert (got[orphan] == SENTINEL).all(), "dispatch wrote a row no valid slot targets"
+    keep = np.flatnonzero(~orphan)
+    assert np.array_equal(got[keep], oracle.dispatch_rows(x, ref["src"], k, keep)), "dispatch rows"
+
+    # combine over the GPU's y (checked elsewhere): a skipped slot adds nothing
+    y_bits = tensor_bits(b.y)
+    out = torch.empty_like(b.out)
+    B.moe_combine(p, b.y, pos_t, b.w, out)
+    torch.cuda.synchronize()
+    want = oracle.combine(with_zero_row(y_bits), pos_zero, ref["w"], k, w.act_dtype)
+    got_o = out.float().cpu().numpy().astype(np.float64)
+    assert not (np.abs(got_o - want) > OUT_ATOL + OUT_RTOL * np.abs(want)).any(), "combine"
+
+    # dispatch backward: a skipped slot adds nothing
+    ds_bits = synth.make_grad(w, 3, n, stream=1)
+    dx = torch.empty(T, H, dtype=act, device="cuda")
+    B.moe_dispatch_backward(p, bits_to_tensor(ds_bits, w.act_dtype).cuda(), pos_t, dx)
+    torch.cuda.synchronize()
+    want = oracle.dispatch_backward(with_zero_row(ds_bits), pos_zero, k, w.act_dtype, T=T)
+    got_x = dx.float().cpu().numpy().astype(np.float64)
+    assert not (np.abs(got_x - want) > OUT_ATOL + OUT_RTOL * np.abs(want)).any(), "dispatch backward"
+
+    # combine backward: no dy row for a skipped slot, its dw exactly 0
+    dout = synth.make_grad(w, 3, T)
+    dy = torch.empty_like(b.y)
+    dy.view(torch.int16).fill_(SENTINEL)
+    dw = torch.full((n,), 7.0, dtype=torch.float32, device="cuda")
+    B.moe_combine_backward(p, bits_to_tensor(dout, w.act_dtype).cuda(), b.y, pos_t, b.w, dy, dw)
+    torch.cuda.synchronize()
+    got_dy = tensor_bits(dy)
+    assert (got_dy[orphan] == SENTINEL).all(), "combine backward wrote a row no valid slot targets"
+    assert np.array_equal(got_dy[keep], oracle.combine_backward_dy(dout, ref["src"], ref["w"], k,
+                                                                   w.act_dtype, keep)), "dy rows"
+    got_dw = host(dw).reshape(T, k).astype(np.float64)
+    assert (got_dw.ravel()[bad] == 0.0).all(), "dw of a skipped slot"
+    want_dw = oracle.combine_backward_dw(with_zero_row(y_bits), dout, pos_zero, k, w.act_dtype)
+    mag = np.stack([(np.abs(oracle.decode16(with_zero_row(y_bits)[pos_zero[np.arange(T) * k + j]],
+                                            w.act_dtype).astype(np.float64))
+                     * np.abs(oracle.decode16(dout, w.act_dtype).astype(np.float64))).sum(1)
+                    for j in range(k)], axis=1)
+    assert not (np.abs(got_dw - want_dw) > H * 2.0 ** -24 * mag + 1e-30).any(), "dw"
+
+
+def test_out_of_range_sources_read_as_expert_zero():
+    rng = np.random.default_rng(12)
+    T, E, k, H, R = 500, 16, 4, 520, 4
+    w = synth.Workload("standin_bad_src", T, E, k, H, R, synth.F16, "none", False)
+    logits, x = synth.make_logits(w, 4), synth.make_x(w, 4)
+    say("[case] out-of-range stand-in sources")
+    ref = oracle.route_and_layout(T, E, k, R, logits)
+    b = run_gpu(w, logits, x, None)
+    n = T * k
+    src_bad, bad = corrupt(ref["src"], n, rng)
+    y = torch.empty_like(b.y)
+    B.moe_expert_standin(B.make_problem(T, E, k, H, R, w.act_dtype), b.send,
+                         torch.from_numpy(src_bad).cuda(), b.idx, y)
+    torch.cuda.synchronize()
+    send_bits = tensor_bits(b.send)
+    experts = np.where(bad, 0, ref["idx"].ravel()[np.where(bad, 0, src_bad)])
+    assert np.array_equal(tensor_bits(y), oracle.expert_standin(send_bits, experts, E, w.act_dtype))
