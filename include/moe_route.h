@@ -149,7 +149,8 @@ moe_status moe_assign_replicas(const moe_problem* p, const int32_t* counts, cons
  * section "Two locality techniques" (a token is sent to a GPU at most once).
  * The send buffer has exactly T*k rows, grouped by destination rank, inside a
  * rank by expert id, inside an expert by token (stable).
- *   idx      i32 [T, k] (read), as written by moe_route
+ *   idx      i32 [T, k] (read), as written by moe_route; an id outside
+ *            [0, E) is clamped into it
  *   assign   i32 [E] or NULL (read): destination of active experts; inactive
  *            experts (-1) and the NULL case use the primary copy
  *   rep, maxrep  as in moe_assign_replicas (NULL: contiguous partition)

@@ -15,6 +15,7 @@ import torch
 import oracle
 import synth
 from combine_router_topk_amd import binding as B
+from combine_router_topk_amd import path as P
 from pathcheck import OUT_ATOL, OUT_RTOL, bits_to_tensor, host, run_gpu, say, tensor_bits
 
 pytestmark = pytest.mark.gpu
@@ -129,3 +130,32 @@ def test_out_of_range_sources_read_as_expert_zero():
     send_bits = tensor_bits(b.send)
     experts = np.where(bad, 0, ref["idx"].ravel()[np.where(bad, 0, src_bad)])
     assert np.array_equal(tensor_bits(y), oracle.expert_standin(send_bits, experts, E, w.act_dtype))
+
+
+@pytest.mark.parametrize("T,E,k,R", [(900, 64, 6, 8), (5000, 256, 8, 32)], ids=["small_batch", "multi_block"])
+def test_out_of_range_expert_ids_are_clamped(T, E, k, R):
+    """The layout kernels clamp an expert id into [0, E): the layout of a
+    corrupted idx equals the oracle's layout of the clamped ids (which may
+    repeat an expert within a token). One workgroup below 8192 pairs, three
+    kernels above."""
+    rng = np.random.default_rng(13)
+    w = synth.Workload("bad_idx", T, E, k, 8, R, synth.BF16, "zipf1.2", False)
+    logits, x = synth.make_logits(w, 5), synth.make_x(w, 5)
+    say(f"[case] out-of-range expert ids T={T} E={E} k={k}")
+    b = run_gpu(w, logits, x, None)
+    idx = host(b.idx).ravel().astype(np.int64)
+    bad = rng.random(idx.shape[0]) < 0.05
+    vals = np.concatenate([BAD_VALUES, [E, E + 3]])
+    idx[bad] = vals[rng.integers(len(vals), size=int(bad.sum()))]
+    b.idx.copy_(torch.from_numpy(idx.astype(np.int32)))
+    P.layout(b)
+    torch.cuda.synchronize()
+    clamped = np.clip(idx, 0, E - 1).reshape(T, k)
+    rank_of = oracle.expert_ranks(E, R, None, None)
+    counts = oracle.demand_vector(clamped, E)
+    eo, ro = oracle.segment_offsets(counts, rank_of, R)
+    pos, src = oracle.permutation(clamped, rank_of)
+    assert np.array_equal(host(b.rank_of), rank_of)
+    assert np.array_equal(host(b.expert_offsets), eo) and np.array_equal(host(b.rank_offsets), ro)
+    assert np.array_equal(host(b.pos), pos) and np.array_equal(host(b.src), src)
+    assert np.array_equal(host(b.dedup), oracle.dedup_counts(clamped, rank_of, R))
