@@ -413,7 +413,8 @@ def graph_leg(P, B, synth, np, torch, dev, steps, seed):
     """The whole path on the replicated decode workload, where every kernel is
     small and the host's launches set the pace: wall time per step for eager
     calls against one replay of a HIP graph holding the same pass (warm
-    cache, the stream drained after each step in both cases)."""
+    cache, the stream drained after each step in both cases), also with
+    route, assign and layout as one call (`fused_plan`)."""
     w = synth.DECODE
     logits, x = synth.make_logits(w, seed), synth.make_x(w, seed)
     rep = synth.replica_table(w)
@@ -421,6 +422,7 @@ def graph_leg(P, B, synth, np, torch, dev, steps, seed):
     b = P.allocate(p, torch.from_numpy(logits), torch.from_numpy(x.view(np.int16)).view(torch.float16),
                    torch.from_numpy(rep), device=dev)
     g = P.capture(b)
+    gf = P.capture(b, P.FUSED_STEPS)
     torch.cuda.synchronize()
 
     def timed(fn):
@@ -435,8 +437,12 @@ def graph_leg(P, B, synth, np, torch, dev, steps, seed):
 
     eager_us = timed(lambda: P.run(b))
     graph_us = timed(g.replay)
+    fused_eager_us = timed(lambda: [step(b) for step in P.FUSED_STEPS])
+    fused_graph_us = timed(gf.replay)
     return {"workload": w.name, "steps": steps, "eager_us_per_step": round(eager_us, 1),
-            "graph_us_per_step": round(graph_us, 1)}
+            "graph_us_per_step": round(graph_us, 1),
+            "fused_plan": {"eager_us_per_step": round(fused_eager_us, 1),
+                           "graph_us_per_step": round(fused_graph_us, 1)}}
 
 
 def path_summary(w, meta_ms: dict, disp_ms: float, comb_ms: float, dc_bytes: int) -> dict:

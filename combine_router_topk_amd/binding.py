@@ -25,7 +25,8 @@ MOE_MAX_E, MOE_MAX_K, MOE_MAX_R, MOE_MAX_REP = 1024, 16, 1024, 16
 MOE_MAX_ROWS = (1 << 24) - 1
 
 EXPORTED = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
-            "moe_route", "moe_assign_replicas", "moe_layout", "moe_layout_single_send",
+            "moe_route", "moe_assign_replicas", "moe_layout", "moe_route_assign_layout",
+            "moe_layout_single_send",
             "moe_single_send_dispatch", "moe_single_send_expand", "moe_dispatch",
             "moe_expert_standin", "moe_combine", "moe_combine_backward", "moe_dispatch_backward",
             "moe_routing_stats", "moe_token_balanced_split")
@@ -63,6 +64,8 @@ def _load() -> ctypes.CDLL:
         "moe_route": (i32, [P, vp, vp, vp, vp, vp, sz, vp]),
         "moe_assign_replicas": (i32, [P, vp, vp, i32, vp, vp, vp]),
         "moe_layout": (i32, [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_route_assign_layout": (i32, [P, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, sz, vp]),
         "moe_layout_single_send": (i32, [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, sz, vp]),
         "moe_single_send_dispatch": (i32, [P, vp, vp, vp, i32, vp]),
@@ -179,6 +182,23 @@ def moe_layout(p: Problem, idx, assign, rep, maxrep: int, rank_of, expert_offset
                            _ptr(pos, torch.int32, n, "pos"), _ptr(src, torch.int32, n, "src"),
                            _ptr(dedup, torch.int32, p.R, "dedup"), _ptr(ws, None, None, "ws"),
                            _nbytes(ws), _stream(stream)), "moe_layout")
+
+
+def moe_route_assign_layout(p: Problem, logits, rep, maxrep: int, idx, w, counts, assign, active,
+                            rank_of, expert_offsets, rank_offsets, pos, src, dedup, ws,
+                            stream=None) -> None:
+    n = p.T * p.k
+    _check(_lib.moe_route_assign_layout(
+        ctypes.byref(p), _ptr(logits, torch.float32, p.T * p.E, "logits"),
+        _ptr(rep, torch.int32, p.E * maxrep if rep is not None else 0, "rep"), maxrep,
+        _ptr(idx, torch.int32, n, "idx"), _ptr(w, torch.float32, n, "w"),
+        _ptr(counts, torch.int32, p.E, "counts"), _ptr(assign, torch.int32, p.E, "assign"),
+        _ptr(active, torch.int32, p.R, "active"), _ptr(rank_of, torch.int32, p.E, "rank_of"),
+        _ptr(expert_offsets, torch.int32, p.E, "expert_offsets"),
+        _ptr(rank_offsets, torch.int32, p.R + 1, "rank_offsets"),
+        _ptr(pos, torch.int32, n, "pos"), _ptr(src, torch.int32, n, "src"),
+        _ptr(dedup, torch.int32, p.R, "dedup"), _ptr(ws, None, None, "ws"), _nbytes(ws),
+        _stream(stream)), "moe_route_assign_layout")
 
 
 def moe_layout_single_send(p: Problem, idx, assign, rep, maxrep: int, rank_of, expert_offsets,

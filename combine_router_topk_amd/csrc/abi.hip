@@ -131,6 +131,41 @@ moe_status moe_assign_replicas(const moe_problem* p, const int32_t* counts, cons
                     fn);
 }
 
+moe_status moe_route_assign_layout(const moe_problem* p, const float* logits, const int32_t* rep,
+                                   int32_t maxrep, int32_t* idx, float* w, int32_t* counts,
+                                   int32_t* assign, int32_t* active, int32_t* rank_of,
+                                   int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos,
+                                   int32_t* src, int32_t* dedup, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  const char* fn = "moe_route_assign_layout";
+  CHECK(check_problem(p, fn));
+  CHECK(check_rep(p, rep, maxrep, fn));
+  CHECK(need(counts, 4, fn, "counts"));
+  CHECK(need(assign, 4, fn, "assign"));
+  CHECK(need(active, 4, fn, "active"));
+  CHECK(need(rank_of, 4, fn, "rank_of"));
+  CHECK(need(expert_offsets, 4, fn, "expert_offsets"));
+  CHECK(need(rank_offsets, 4, fn, "rank_offsets"));
+  CHECK(need(dedup, 4, fn, "dedup"));
+  CHECK(need(ws, 256, fn, "ws"));
+  if (p->T > 0) {
+    CHECK(need(logits, 4, fn, "logits"));
+    CHECK(need(idx, 4, fn, "idx"));
+    CHECK(need(w, 4, fn, "w"));
+    CHECK(need(pos, 4, fn, "pos"));
+    CHECK(need(src, 4, fn, "src"));
+  }
+  const size_t req = moe::workspace_bytes(p->T, p->E, p->R);
+  if (ws_bytes < req) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, req);
+  clear_stale_error();
+  return hip_status(moe::launch_route_assign_layout(
+                        logits, p->T, p->E, p->k, p->R, rep, maxrep,
+                        (p->flags & MOE_FLAG_GREEDY_ID_ORDER) != 0, idx, w, counts, assign, active,
+                        rank_of, expert_offsets, rank_offsets, pos, src, dedup,
+                        static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 moe_status moe_layout(const moe_problem* p, const int32_t* idx, const int32_t* assign,
                       const int32_t* rep, int32_t maxrep, int32_t* rank_of,
                       int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos, int32_t* src,

@@ -35,6 +35,20 @@ size_t workspace_bytes(int T, int E, int R);
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                         int32_t* counts, int32_t* ws, hipStream_t s);
 
+// The top-k kernel of launch_route alone: idx, w, and one histogram row per
+// route block in ws ([blocking_for(T, E, R).route_nblk, E]), no counts.
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                             int32_t* ws, hipStream_t s);
+
+// route, assign and layout of one batch: for a small batch the top-k kernel
+// and one workgroup that does everything else, else the three launches.
+hipError_t launch_route_assign_layout(const float* logits, int T, int E, int k, int R,
+                                      const int32_t* rep, int maxrep, bool id_order, int32_t* idx,
+                                      float* w, int32_t* counts, int32_t* assign, int32_t* active,
+                                      int32_t* rank_of, int32_t* expert_offsets,
+                                      int32_t* rank_offsets, int32_t* pos, int32_t* src,
+                                      int32_t* dedup, int32_t* ws, hipStream_t s);
+
 hipError_t launch_assign(const int32_t* counts, int E, int R, const int32_t* rep, int maxrep,
                          bool id_order, int32_t* assign, int32_t* active, hipStream_t s);
 

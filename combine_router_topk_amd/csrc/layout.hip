@@ -31,6 +31,7 @@
 // A small batch (T k <= 8192 pairs) runs all of it in one workgroup instead
 // (layout_small), sharing the same device functions.
 #include "device.hpp"
+#include "greedy.hpp"
 #include "launch.hpp"
 
 namespace moe {
@@ -426,19 +427,25 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_single_send_kernel(
 // The whole layout of a small batch (T k <= kSmallPairs) in one workgroup:
 // counts, plan, permutation and single-send rows, every table in LDS, with
 // the same device code as the multi-block kernels. A decode batch then
-// takes one launch instead of three or four.
+// takes one launch instead of three or four. `assign` may point to global
+// memory or LDS. smem holds small_layout_ints(E, R) ints.
 constexpr int kSmallPairs = 8192;
+constexpr int kSmallLdsInts = 16 * 1024 - 64;  // dynamic LDS under 64 KiB beside 128 static bytes
 
-__global__ __launch_bounds__(kPlanThreads) void layout_small_kernel(
-    const int32_t* __restrict__ idx, int T, int E, int k, int R,
-    const int32_t* __restrict__ assign, const int32_t* __restrict__ rep, int maxrep,
-    int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
-    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pos, int32_t* __restrict__ src,
-    int32_t* __restrict__ dedup, int32_t* __restrict__ ss_rank_offsets,
-    int32_t* __restrict__ ss_row, int32_t* __restrict__ ss_token, int32_t* __restrict__ lead) {
-  extern __shared__ __align__(16) int smem[];
-  __shared__ int s_wave[kPlanWaves];
-  __shared__ int s_wave2[kPlanWaves];
+__host__ __device__ constexpr int small_layout_ints(int E, int R) {
+  // s_rank, s_cnt (E rounded up for the plan's padding), four [R] tables,
+  // run[M] and the two [16][M] wave tables, M = max(E, R)
+  return 2 * ((E + 8) & ~7) + 4 * R + (1 + 2 * kPlanWaves) * (E > R ? E : R);
+}
+
+__device__ __forceinline__ void layout_small_block(
+    const int32_t* __restrict__ idx, int T, int E, int k, int R, const int32_t* assign,
+    const int32_t* __restrict__ rep, int maxrep, int32_t* __restrict__ rank_of,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_offsets,
+    int32_t* __restrict__ pos, int32_t* __restrict__ src, int32_t* __restrict__ dedup,
+    int32_t* __restrict__ ss_rank_offsets, int32_t* __restrict__ ss_row,
+    int32_t* __restrict__ ss_token, int32_t* __restrict__ lead, int* smem, int* s_wave,
+    int* s_wave2) {
   const int ep = (E + 8) & ~7;  // room for the plan's padding to a multiple of 8
   const int M = E > R ? E : R;
   int* s_rank = smem;            // [ep]
@@ -475,6 +482,80 @@ __global__ __launch_bounds__(kPlanThreads) void layout_small_kernel(
                                  lead, ss_row, ss_token);
 }
 
+__global__ __launch_bounds__(kPlanThreads) void layout_small_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int R,
+    const int32_t* __restrict__ assign, const int32_t* __restrict__ rep, int maxrep,
+    int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pos, int32_t* __restrict__ src,
+    int32_t* __restrict__ dedup, int32_t* __restrict__ ss_rank_offsets,
+    int32_t* __restrict__ ss_row, int32_t* __restrict__ ss_token, int32_t* __restrict__ lead) {
+  extern __shared__ __align__(16) int smem[];
+  __shared__ int s_wave[kPlanWaves];
+  __shared__ int s_wave2[kPlanWaves];
+  layout_small_block(idx, T, E, k, R, assign, rep, maxrep, rank_of, expert_offsets, rank_offsets,
+                     pos, src, dedup, ss_rank_offsets, ss_row, ss_token, lead, smem, s_wave,
+                     s_wave2);
+}
+
+// The routing plan of a small batch after the top-k kernel, in one
+// workgroup: the demand vector as the column sums of the route's per-block
+// histogram rows, the greedy replica assignment (greedy.hpp) and the whole
+// layout, with the counts and the assignment kept in LDS between the steps.
+// Outputs equal those of the separate column-sum, assignment and layout
+// kernels. Dynamic LDS: counts [E] and assign [E], then a region the
+// assignment's scratch and the layout's tables use in turn.
+__host__ __device__ constexpr int plan_greedy_ints(int E, int R) {
+  // act (at least 64 entries), ncand (E bytes), cand (E * kMaxRep halves)
+  return (R > kWave ? R : kWave) + (E + 3) / 4 + E * kMaxRep / 2;
+}
+
+__host__ __device__ constexpr int plan_small_ints(int E, int R) {
+  const int g = plan_greedy_ints(E, R), l = small_layout_ints(E, R);
+  return 2 * ((E + 3) & ~3) + (g > l ? g : l);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void route_plan_small_kernel(
+    const int32_t* __restrict__ hist, int nblk, const int32_t* __restrict__ idx, int T, int E,
+    int k, int R, const int32_t* __restrict__ rep, int maxrep, int id_order,
+    int32_t* __restrict__ counts, int32_t* __restrict__ assign, int32_t* __restrict__ active,
+    int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pos, int32_t* __restrict__ src,
+    int32_t* __restrict__ dedup) {
+  extern __shared__ __align__(16) int smem[];
+  __shared__ int s_wave[kPlanWaves];
+  __shared__ int s_wave2[kPlanWaves];
+  const int e4 = (E + 3) & ~3;
+  int* s_counts = smem;            // [E]
+  int* s_assign = smem + e4;       // [E]
+  int* region = smem + 2 * e4;     // greedy scratch, then the layout's tables
+  const int tid = threadIdx.x;
+  // demand vector: column sums of the [nblk, E] histogram rows, the rows
+  // split among max(1, 1024 / E) thread groups per column (integer adds)
+  for (int e = tid; e < E; e += blockDim.x) s_counts[e] = 0;
+  __syncthreads();
+  {
+    const int groups = E >= kPlanThreads ? 1 : kPlanThreads / E;
+    const int g = tid / E;
+    for (int e = tid % E; g < groups && e < E; e += kPlanThreads) {
+      int acc = 0;
+      for (int r = g; r < nblk; r += groups) acc += hist[(size_t)r * E + e];
+      atomicAdd(&s_counts[e], acc);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) counts[e] = s_counts[e];
+  // greedy replica assignment into LDS
+  int* act = region;
+  unsigned char* ncand = reinterpret_cast<unsigned char*>(region + (R > kWave ? R : kWave));
+  unsigned short* cand = reinterpret_cast<unsigned short*>(region + (R > kWave ? R : kWave) + (E + 3) / 4);
+  assign_block(s_counts, E, R, rep, maxrep, id_order, s_assign, act, ncand, cand);
+  for (int e = tid; e < E; e += blockDim.x) assign[e] = s_assign[e];
+  for (int g = tid; g < R; g += blockDim.x) active[g] = act[g];
+  __syncthreads();  // the region is reused below
+  layout_small_block(idx, T, E, k, R, s_assign, rep, maxrep, rank_of, expert_offsets, rank_offsets,
+                     pos, src, dedup, nullptr, nullptr, nullptr, nullptr, region, s_wave, s_wave2);
+}
+
 }  // namespace
 
 hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const int32_t* assign,
@@ -489,10 +570,9 @@ hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const i
   int32_t* ded = ws + (size_t)bl.layout_nblk * E;       // [nblk, R]
   int32_t* lead = ded + (size_t)bl.layout_nblk * R;     // [T] leader masks (single-send)
   {
-    const int ep = (E + 8) & ~7, M = E > R ? E : R;
-    const size_t small_ints = 2 * ep + 4 * R + (1 + 2 * kPlanWaves) * M;
+    const size_t small_ints = small_layout_ints(E, R);
     // dynamic LDS under 64 KiB with room for the kernel's static 128 bytes
-    if (T > 0 && (int64_t)T * k <= kSmallPairs && small_ints <= 16 * 1024 - 64) {
+    if (T > 0 && (int64_t)T * k <= kSmallPairs && small_ints <= kSmallLdsInts) {
       layout_small_kernel<<<1, kPlanThreads, small_ints * sizeof(int), s>>>(
           idx, T, E, k, R, assign, rep, maxrep, rank_of, expert_offsets, rank_offsets, pos, src,
           dedup, ss_rank_offsets, ss_row, ss_token, lead);
@@ -528,6 +608,30 @@ hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const i
     layout_single_send_kernel<4><<<nblk, 4 * kWave, (E + 9 * R) * sizeof(int), s>>>(
         idx, T, E, k, R, bl.layout_tpb, rank_of, ded, ss_rank_offsets, lead, ss_row, ss_token);
   return hipGetLastError();
+}
+
+hipError_t launch_route_assign_layout(const float* logits, int T, int E, int k, int R,
+                                      const int32_t* rep, int maxrep, bool id_order, int32_t* idx,
+                                      float* w, int32_t* counts, int32_t* assign, int32_t* active,
+                                      int32_t* rank_of, int32_t* expert_offsets,
+                                      int32_t* rank_offsets, int32_t* pos, int32_t* src,
+                                      int32_t* dedup, int32_t* ws, hipStream_t s) {
+  const size_t plan_ints = plan_small_ints(E, R);
+  if (T > 0 && (int64_t)T * k <= kSmallPairs && plan_ints <= kSmallLdsInts) {
+    hipError_t err = launch_route_topk(logits, T, E, k, idx, w, ws, s);
+    if (err != hipSuccess) return err;
+    route_plan_small_kernel<<<1, kPlanThreads, plan_ints * sizeof(int), s>>>(
+        ws, blocking_for(T, E, R).route_nblk, idx, T, E, k, R, rep, rep ? maxrep : 1,
+        id_order ? 1 : 0, counts, assign, active, rank_of, expert_offsets, rank_offsets, pos, src,
+        dedup);
+    return hipGetLastError();
+  }
+  hipError_t err = launch_route(logits, T, E, k, idx, w, counts, ws, s);
+  if (err != hipSuccess) return err;
+  err = launch_assign(counts, E, R, rep, rep ? maxrep : 1, id_order, assign, active, s);
+  if (err != hipSuccess) return err;
+  return launch_layout(idx, T, E, k, R, assign, rep, rep ? maxrep : 1, rank_of, expert_offsets,
+                       rank_offsets, pos, src, dedup, nullptr, nullptr, nullptr, ws, s);
 }
 
 }  // namespace moe

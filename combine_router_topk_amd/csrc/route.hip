@@ -299,23 +299,27 @@ size_t workspace_bytes(int T, int E, int R) {
   return n < 256 ? 256 : n;
 }
 
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                             int32_t* ws, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const Blocking b = blocking_for(T, E, 1);
+  const int L = lanes_per_token(E);
+  const int V = (E + L - 1) / L;  // L = 16: 1..4; 32: 3..4; 64: 3..16
+  const int tpb = b.route_tpb, n = b.route_nblk;
+  if (L == 16 && V == 1) return launch_topk<16, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
+  if (L == 16 && V == 2) return launch_topk<16, 2>(logits, T, E, k, tpb, n, idx, w, ws, s);
+  if (L == 16) return launch_topk<16, 4>(logits, T, E, k, tpb, n, idx, w, ws, s);
+  if (L == 32) return launch_topk<32, 4>(logits, T, E, k, tpb, n, idx, w, ws, s);
+  if (V <= 4) return launch_wave<4>(logits, T, E, k, tpb, n, idx, w, ws, s);
+  if (V <= 8) return launch_wave<8>(logits, T, E, k, tpb, n, idx, w, ws, s);
+  return launch_wave<16>(logits, T, E, k, tpb, n, idx, w, ws, s);
+}
+
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                         int32_t* counts, int32_t* ws, hipStream_t s) {
   const Blocking b = blocking_for(T, E, 1);
-  hipError_t err = hipSuccess;
-  if (T > 0) {
-    const int L = lanes_per_token(E);
-    const int V = (E + L - 1) / L;  // L = 16: 1..4; 32: 3..4; 64: 3..16
-    const int tpb = b.route_tpb, n = b.route_nblk;
-    if (L == 16 && V == 1) err = launch_topk<16, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else if (L == 16 && V == 2) err = launch_topk<16, 2>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else if (L == 16) err = launch_topk<16, 4>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else if (L == 32) err = launch_topk<32, 4>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else if (V <= 4) err = launch_wave<4>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else if (V <= 8) err = launch_wave<8>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    else err = launch_wave<16>(logits, T, E, k, tpb, n, idx, w, ws, s);
-    if (err != hipSuccess) return err;
-  }
+  const hipError_t err = launch_route_topk(logits, T, E, k, idx, w, ws, s);
+  if (err != hipSuccess) return err;
   const int rows = T > 0 ? b.route_nblk : 0;
   column_sum_kernel<<<(E + kWave - 1) / kWave, 1024, 0, s>>>(ws, rows, E, counts);
   return hipGetLastError();

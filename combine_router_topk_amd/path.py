@@ -75,6 +75,14 @@ def layout(b: Buffers, stream=None) -> None:
                  b.rank_offsets, b.pos, b.src, b.dedup, b.ws, stream)
 
 
+def route_assign_layout(b: Buffers, stream=None) -> None:
+    """route, assign and layout in one library call (two launches for a
+    decode-sized batch)."""
+    B.moe_route_assign_layout(b.p, b.logits, b.rep, b.maxrep, b.idx, b.w, b.counts, b.assign,
+                              b.active, b.rank_of, b.expert_offsets, b.rank_offsets, b.pos, b.src,
+                              b.dedup, b.ws, stream)
+
+
 def dispatch(b: Buffers, stream=None) -> None:
     B.moe_dispatch(b.p, b.x, b.pos, b.send, stream)
 
@@ -88,6 +96,8 @@ def combine(b: Buffers, stream=None) -> None:
 
 
 STEPS = (route, assign, layout, dispatch, standin, combine)
+# the same pass with route, assign and layout in one call
+FUSED_STEPS = (route_assign_layout, dispatch, standin, combine)
 
 
 def run(b: Buffers, stream=None) -> None:

@@ -188,6 +188,23 @@ moe_status moe_layout_single_send(const moe_problem* p, const int32_t* idx, cons
                                   int32_t* ss_row, int32_t* ss_token, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/* moe_route, moe_assign_replicas and moe_layout in one call, with the same
+ * arguments and outputs as those three calls made in that order (assign is
+ * both an output and the layout's input). For a decode batch fixed latency
+ * rather than bytes sets the time ([METRO] section "Find the crossover
+ * instead of copying 2 MB": below the crossover payload a fixed overhead
+ * dominates), so the steps share launches. A batch with T*k <= 8192 whose tables fit in 64 KiB
+ * of LDS takes two launches: the top-k kernel, then one workgroup that sums
+ * the demand vector, runs the greedy and lays out the batch. Larger batches
+ * take the kernels of the three separate calls. ws is one workspace of
+ * moe_workspace_bytes().                                                   */
+moe_status moe_route_assign_layout(const moe_problem* p, const float* logits, const int32_t* rep,
+                                   int32_t maxrep, int32_t* idx, float* w, int32_t* counts,
+                                   int32_t* assign, int32_t* active, int32_t* rank_of,
+                                   int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos,
+                                   int32_t* src, int32_t* dedup, void* ws, size_t ws_bytes,
+                                   void* stream);
+
 /* Single-send dispatch: each token row x[t] is copied once to each distinct
  * single-send row among ss_row[t*k .. t*k+k). [CORR] section "Two locality
  * techniques".

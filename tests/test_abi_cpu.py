@@ -188,3 +188,33 @@ def test_binding_hands_missing_buffers_to_the_library_checks():
     # a single-send buffer of no rows has capacity 0: nothing is written
     B.moe_single_send_dispatch(p, None, None, None, stream=0)
     B.moe_single_send_expand(p, *(None,) * 6, stream=0)
+
+
+def test_route_assign_layout_rejects_bad_arguments_before_any_launch():
+    p = prob()
+    ref = ctypes.byref(p)
+    lib = B._lib
+    fake = ctypes.c_void_p(1 << 20)
+    ws = 1 << 20
+
+    def call(logits=fake, rep=None, maxrep=1, idx=fake, w=fake, counts=fake, assign=fake,
+             active=fake, rank_of=fake, eo=fake, ro=fake, pos=fake, src=fake, dedup=fake,
+             wsp=fake, wsb=ws, pp=ref):
+        return lib.moe_route_assign_layout(pp, logits, rep, maxrep, idx, w, counts, assign, active,
+                                           rank_of, eo, ro, pos, src, dedup, wsp, wsb, None)
+    for field in ("logits", "idx", "w", "counts", "assign", "active", "rank_of", "pos", "src",
+                  "dedup"):
+        assert call(**{field: None}) == B.MOE_ERR_INVALID_ARG, field
+        assert field in B.moe_last_error()
+    assert call(eo=None) == B.MOE_ERR_INVALID_ARG and "expert_offsets" in B.moe_last_error()
+    assert call(ro=None) == B.MOE_ERR_INVALID_ARG and "rank_offsets" in B.moe_last_error()
+    assert call(wsp=None) == B.MOE_ERR_INVALID_ARG and "ws" in B.moe_last_error()
+    assert call(wsb=16) == B.MOE_ERR_WORKSPACE
+    assert call(rep=fake, maxrep=0) == B.MOE_ERR_INVALID_ARG and "maxrep" in B.moe_last_error()
+    p2 = prob(E=12, R=5)  # no replica table: R must divide E
+    assert call(pp=ctypes.byref(p2)) == B.MOE_ERR_INVALID_ARG
+    # an empty batch needs no logits, idx, w, pos or src (nothing is launched here:
+    # the workspace size is checked first and is too small)
+    p0 = prob(T=0)
+    assert call(pp=ctypes.byref(p0), logits=None, idx=None, w=None, pos=None, src=None,
+                wsb=0) == B.MOE_ERR_WORKSPACE
