@@ -223,6 +223,28 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
+// One token's k (<= kMaxK) entries of a [T, k] int table, read so that every
+// load is issued before any is used: the bucket of k is a uniform branch,
+// and inside it the loads are unconditional (slots from k on reread slot
+// k - 1, and callers ignore them), so one wait covers them all. Loads behind
+// a per-slot condition were each waited for in turn (statistics count kernel
+// at T = 65536, k = 8: 28.8 us that way, 24.8 us with this).
+template <int N>
+__device__ __forceinline__ void load_slots_n(const int32_t* __restrict__ row, int k,
+                                             int (&v)[kMaxK]) {
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) v[j] = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = row[j < k ? j : k - 1];
+}
+
+__device__ __forceinline__ void load_slots(const int32_t* __restrict__ row, int k, int (&v)[kMaxK]) {
+  if (k <= 2) load_slots_n<2>(row, k, v);
+  else if (k <= 4) load_slots_n<4>(row, k, v);
+  else if (k <= 8) load_slots_n<8>(row, k, v);
+  else load_slots_n<kMaxK>(row, k, v);
+}
+
 // Destination rank of expert e: its assigned replica if active, else its
 // primary copy, else the contiguous partition. Clamped so a bad table can
 // never index out of bounds.

@@ -58,10 +58,11 @@ __device__ void count_tokens(const int32_t* __restrict__ idx, int t0, int t1, in
   for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
     // ranks of the token's k experts in registers, then one count per
     // distinct rank (the first slot that reaches it)
-    const int32_t* row = idx + (size_t)t * k;
+    int ids[kMaxK];
+    load_slots(idx + (size_t)t * k, k, ids);
     int rk[kMaxK];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) rk[j] = j < k ? s_rank[clamp_expert(row[j], E)] : -1 - j;
+    for (int j = 0; j < kMaxK; ++j) rk[j] = j < k ? s_rank[clamp_expert(ids[j], E)] : -1 - j;
     int lead = 0;  // bit j: slot j is the token's first slot on its rank
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {

@@ -79,10 +79,10 @@ __global__ __launch_bounds__(kStatThreads) void stats_count_kernel(
   const int t0 = blockIdx.x * tpb;
   const int t1 = min(T, t0 + tpb);
   for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
-    const int32_t* row = idx + (size_t)t * k;
     int e[kMaxK];
+    load_slots(idx + (size_t)t * k, k, e);
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) e[j] = j < k ? clamp_id(row[j], E) : 0;
+    for (int j = 0; j < kMaxK; ++j) e[j] = j < k ? clamp_id(e[j], E) : 0;
     if (do_s) {
       const int src = static_cast<int>((int64_t)t * R / T);
 #pragma unroll
