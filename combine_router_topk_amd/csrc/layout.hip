@@ -49,7 +49,7 @@ __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (
 // token, its distinct destination ranks (s_ded); with lead_mask, bit j of
 // lead_mask[t] marks slot j as the token's first slot on its rank. All
 // threads of the block take part.
-__device__ void count_tokens(const int32_t* __restrict__ idx, int t0, int t1, int E, int k,
+__device__ __forceinline__ void count_tokens(const int32_t* __restrict__ idx, int t0, int t1, int E, int k,
                              const int* s_rank, int* s_hist, int* s_ded,
                              int32_t* __restrict__ lead_mask) {
   const size_t i0 = (size_t)t0 * k, i1 = (size_t)t1 * k;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
 // each task's waves splitting the rows into segments of at most kSegRegs
 // rows (the layout blocking guarantees it), loaded in one batch and kept in
 // registers: one memory round trip per group of tasks.
-__device__ void column_pass(int32_t* __restrict__ hist, int E, int32_t* __restrict__ ded, int R,
+__device__ __forceinline__ void column_pass(int32_t* __restrict__ hist, int E, int32_t* __restrict__ ded, int R,
                             int rows, int* s_cnt, int* s_ded, int (*part)[kWave]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -161,7 +161,7 @@ __device__ void column_pass(int32_t* __restrict__ hist, int E, int32_t* __restri
 
 // Exclusive prefix sum of one value per thread over the whole block (1024
 // threads); returns the prefix and writes the block total to *total.
-__device__ int block_excl_scan(int v, int* s_wave, int* total) {
+__device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int incl = wave_incl_scan(v, lane);
@@ -186,7 +186,7 @@ __device__ int block_excl_scan(int v, int* s_wave, int* total) {
 // single-send rank offsets. s_rank and s_cnt must have room for E rounded up
 // to 8. Optional LDS copies: s_eoff[E] of the expert offsets, s_ssoff[R] of
 // the single-send offsets. All threads of the (1024-thread) block take part.
-__device__ void plan_finish(int E, int R, int* s_rank, int* s_cnt, const int* s_ded, int* s_rtok,
+__device__ __forceinline__ void plan_finish(int E, int R, int* s_rank, int* s_cnt, const int* s_ded, int* s_rtok,
                             int* s_roff, int* s_wave, int* s_wave2, int32_t* __restrict__ rank_of,
                             int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_offsets,
                             int32_t* __restrict__ dedup, int32_t* __restrict__ ss_rank_offsets,
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kPlanThreads) void layout_plan_kernel(
 // src[pos] = flat pair index. All WAVES * 64 threads take part; ends with a
 // barrier.
 template <int WAVES>
-__device__ void permute_rounds(const int32_t* __restrict__ idx, int64_t i0, int64_t i1, int E,
+__device__ __forceinline__ void permute_rounds(const int32_t* __restrict__ idx, int64_t i0, int64_t i1, int E,
                                int n_items, int* run, int* wcnt, int* wtag,
                                int32_t* __restrict__ pos, int32_t* __restrict__ src) {
   constexpr int kThreads = WAVES * kWave;
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_permute_kernel(
 // leader's row is the number of leaders of its rank before it; a non-leader
 // sees its own leader among those before it, so its row is that count - 1.
 template <int WAVES>
-__device__ void single_send_rounds(const int32_t* __restrict__ idx, int64_t i0, int64_t i1, int k,
+__device__ __forceinline__ void single_send_rounds(const int32_t* __restrict__ idx, int64_t i0, int64_t i1, int k,
                                    int E, int R, int n_items, const int* s_rank, int* run,
                                    int* wcnt, int* wtag, const int32_t* __restrict__ lead_mask,
                                    int32_t* __restrict__ ss_row, int32_t* __restrict__ ss_token) {

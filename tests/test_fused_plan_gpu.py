@@ -65,6 +65,28 @@ def test_small_batches_without_table(w):
     run_both(w, 1)
 
 
+# Larger batches run the three calls' kernels under the one call.
+@pytest.mark.parametrize("w", [synth.TRAIN_TOP2, synth.TRAIN_TOP6,
+                               synth.scaled(synth.TRAIN_TOP2, T=9001),
+                               synth.Workload("E48_k5_R12", 12000, 48, 5, 8, 12, synth.BF16, "zipf1.2", False),
+                               synth.Workload("E64_k16_R64", 20000, 64, 16, 8, 64, synth.BF16, "zipf1.2", False)],
+                         ids=lambda w: w.name)
+def test_larger_batches(w):
+    run_both(w, 2)
+
+
+@pytest.mark.parametrize("order", ["constrained", "id"])
+def test_larger_batch_with_replica_table(order):
+    rng = np.random.default_rng(77)
+    E, R, maxrep = 64, 16, 4
+    rep = np.full((E, maxrep), -1, np.int32)
+    for e in range(E):
+        n = int(rng.integers(1, maxrep + 1))
+        rep[e, :n] = rng.choice(R, size=n, replace=False)
+    w = synth.Workload("fused_large_rep", 12000, E, 4, 8, R, synth.BF16, "cluster_pairs", False)
+    run_both(w, 3, rep=rep, order=order)
+
+
 @pytest.mark.parametrize("order", ["constrained", "id"])
 @pytest.mark.parametrize("E,R,maxrep,T,k", [(64, 8, 3, 500, 4), (256, 128, 3, 600, 8),
                                             (100, 7, 5, 300, 6)],
