@@ -119,28 +119,39 @@ __global__ __launch_bounds__(kStatThreads) void stats_count_kernel(
       if (s_C[i] != 0) atomicAdd(&C[(size_t)a0 * E + i], s_C[i]);
 }
 
-__device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* s_red) {
+// Block sums of three 64-bit integers at once: the three butterflies are
+// independent, so their exchanges overlap, and one barrier serves all three.
+__device__ __forceinline__ void block_sum3_i64(int64_t (&v)[3], int64_t (*s_red)[3]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  for (int off = kWave / 2; off > 0; off /= 2) v += __shfl_xor(v, off);
-  if (lane == 0) s_red[wave] = v;
+  for (int off = kWave / 2; off > 0; off /= 2) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) v[i] += __shfl_xor(v[i], off);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) s_red[wave][i] = v[i];
+  }
   __syncthreads();
-  int64_t all = 0;
-  for (int w = 0; w < kFinalThreads / kWave; ++w) all += s_red[w];
-  __syncthreads();
-  return all;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    int64_t all = 0;
+    for (int w = 0; w < kFinalThreads / kWave; ++w) all += s_red[w][i];
+    v[i] = all;
+  }
 }
 
 __global__ __launch_bounds__(kFinalThreads) void stats_finalize_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ S, int T, int E, int k, int R,
     double* __restrict__ stats) {
   __shared__ int64_t s_load[kMaxR];
-  __shared__ int64_t s_red[kFinalThreads / kWave];
+  __shared__ int64_t s_red[kFinalThreads / kWave][3];
   __shared__ int s_part[kFinalThreads];
   const int tid = threadIdx.x;  // E, R <= 1024 == blockDim.x
   const int64_t N = (int64_t)T * k;
   int64_t my_max = 0, diag = 0, load = 0;
   if (tid < E) my_max = counts[tid];
+  if (tid < R) diag = S[(size_t)tid * R + tid];  // in flight with the column loads
   // column sums of S: G = 1024 / R groups of rows, each thread summing one
   // column over its group's rows with several loads in flight, then the
   // group partials added in order
@@ -156,7 +167,6 @@ __global__ __launch_bounds__(kFinalThreads) void stats_finalize_kernel(
   if (tid < R) {
     for (int g = 0; g < G; ++g) load += s_part[g * R + tid];
     s_load[tid] = load;
-    diag = S[(size_t)tid * R + tid];
   }
   __syncthreads();
   // block maximum of the counts
@@ -178,9 +188,9 @@ __global__ __launch_bounds__(kFinalThreads) void stats_finalize_kernel(
     }
     sq = load * load;
   }
-  const int64_t trace = block_sum_i64(diag, s_red);
-  const int64_t gini_num = block_sum_i64(absdiff, s_red);
-  const int64_t sum_sq = block_sum_i64(sq, s_red);
+  int64_t sums[3] = {diag, absdiff, sq};
+  block_sum3_i64(sums, s_red);
+  const int64_t trace = sums[0], gini_num = sums[1], sum_sq = sums[2];
   if (tid == 0) {
     const double nan = __builtin_nan("");
     if (N == 0) {
