@@ -207,6 +207,18 @@ __device__ __forceinline__ double group_sum16_f64(double x) {
   return x;
 }
 
+// Sum over each aligned group of KP lanes (KP in {1, 2, 4, 8, 16}); every
+// lane of the group receives it. Fixed tree order, so the result is
+// deterministic.
+template <int KP>
+__device__ __forceinline__ double group_sum_f64(double x) {
+  if constexpr (KP >= 2) x += dpp_f64<kDppXor1>(x);
+  if constexpr (KP >= 4) x += dpp_f64<kDppXor2>(x);
+  if constexpr (KP >= 8) x += dpp_f64<kDppHalfMirror>(x);
+  if constexpr (KP >= 16) x += dpp_f64<kDppMirror>(x);
+  return x;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll

@@ -130,7 +130,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 // matching slot, a masked clear, and a select that records the choice in
 // lane j. Everything that decides the selection is wave-uniform, so the
 // scalar unit does little and the vector unit only O(V) work per round.
-template <int V>
+// The fp64 softmax waits until 64 / KP tokens have been selected (KP = k
+// rounded up to a power of two): token s of a batch keeps its slot j in lane
+// s KP + j, and one fp64 pass evaluates the whole batch. Evaluated per token,
+// the softmax used k of the 64 lanes for the cost of all.
+template <int V, int KP>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_wave_kernel(
     const float* __restrict__ logits, int T, int E, int k, int tpb, int32_t* __restrict__ idx,
     float* __restrict__ w, int32_t* __restrict__ block_hist) {
@@ -164,6 +168,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_wave_kernel(
     }
   };
 
+  constexpr int kBatch = kWave / KP;  // tokens per softmax batch
+  int slot = 0;                        // the current token's place in the batch
+  uint32_t b_e = 0u, b_key = 0u, b_top = 0u;
+  int b_t = 0;
+  auto flush = [&](int filled) {
+    const int j = lane % KP;
+    const bool on = lane / KP < filled && j < k;
+    double ex = 0.0;
+    if (on) ex = exp(static_cast<double>(key_logit(b_key)) - static_cast<double>(key_logit(b_top)));
+    const double sum = group_sum_f64<KP>(ex);  // lanes j >= k hold 0
+    if (on) {
+      const size_t o = (size_t)b_t * k + j;
+      idx[o] = static_cast<int32_t>(b_e);
+      w[o] = static_cast<float>(ex / sum);
+      atomicAdd(&s_hist[b_e], 1);
+    }
+  };
+
   float nxt[V];
   load_row(t_begin + wave, nxt);
   for (int t = t_begin + wave; t < t_end; t += nwaves) {
@@ -172,7 +194,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_wave_kernel(
     for (int v = 0; v < V; ++v) key[v] = (e0 + v < E) ? logit_key(nxt[v]) : 0u;
     load_row(t + nwaves, nxt);  // the wave's next token, in flight meanwhile
 
-    uint32_t my_e = 0u, my_key = 0u, top_key = 0u;
+    uint32_t top_key = 0u;
     for (int j = 0; j < k; ++j) {
       uint32_t lm = key[0];
 #pragma unroll
@@ -187,25 +209,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_wave_kernel(
       for (int v = 0; v < V; ++v)
         if (v == fvs) key[v] = lane == l ? 0u : key[v];  // taken: never chosen again
       const int e_sel = l * V + fvs;
-      if (lane == j) {
-        my_e = static_cast<uint32_t>(e_sel);
-        my_key = best;
+      if (lane == slot * KP + j) {
+        b_e = static_cast<uint32_t>(e_sel);
+        b_key = best;
       }
       if (j == 0) top_key = best;
     }
-
-    // softmax over the k selected logits in fp64, lanes 0..k-1
-    double ex = 0.0;
-    if (lane < k) ex = exp(static_cast<double>(key_logit(my_key)) -
-                           static_cast<double>(key_logit(top_key)));
-    const double sum = group_sum16_f64<kWave>(ex);  // lanes >= k hold 0
-    if (lane < k) {
-      const size_t o = (size_t)t * k + lane;
-      idx[o] = static_cast<int32_t>(my_e);
-      w[o] = static_cast<float>(ex / sum);
-      atomicAdd(&s_hist[my_e], 1);
+    if (lane / KP == slot) {
+      b_top = top_key;
+      b_t = t;
+    }
+    if (++slot == kBatch) {  // softmax over the k selected logits of each token, in fp64
+      flush(kBatch);
+      slot = 0;
     }
   }
+  if (slot > 0) flush(slot);
   __syncthreads();
   int32_t* row = block_hist + (size_t)blockIdx.x * E;
   for (int e = threadIdx.x; e < E; e += blockDim.x) row[e] = s_hist[e];
@@ -252,7 +271,12 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int tpb, int nb
 template <int V>
 hipError_t launch_wave(const float* logits, int T, int E, int k, int tpb, int nblk, int32_t* idx,
                        float* w, int32_t* ws, hipStream_t s) {
-  route_topk_wave_kernel<V><<<nblk, kRouteThreads, E * sizeof(int), s>>>(logits, T, E, k, tpb, idx, w, ws);
+  const size_t lds = E * sizeof(int);
+  if (k <= 1) route_topk_wave_kernel<V, 1><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
+  else if (k <= 2) route_topk_wave_kernel<V, 2><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
+  else if (k <= 4) route_topk_wave_kernel<V, 4><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
+  else if (k <= 8) route_topk_wave_kernel<V, 8><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
+  else route_topk_wave_kernel<V, 16><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
   return hipGetLastError();
 }
 
