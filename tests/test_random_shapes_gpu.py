@@ -1,4 +1,5 @@
-"""GPU parity on seeded random problem shapes: every entry point, called
+"""GPU parity on seeded random problem shapes: every entry point (the
+one-call route + assignment + layout against the separate calls), called
 through the C ABI, against the CPU oracle on shapes drawn across the whole
 documented range (E from 1 to 1024 log-uniform, k up to min(E, 16), R a
 divisor of E or any R up to 1024 with a random replica table, rows from one
@@ -19,6 +20,7 @@ from combine_router_topk_amd import binding as B
 from pathcheck import say
 from test_backward_gpu import run_backward
 from test_eplb_gpu import random_table, run_split
+from test_fused_plan_gpu import run_both
 from test_parity_gpu import run_and_check
 from test_single_send_gpu import check_single_send, run_single_send
 from test_stats_gpu import run_stats
@@ -97,6 +99,8 @@ def test_random_problem_every_entry_point(c):
     x = synth.make_x(w, c["seed"] % 1000)
     # forward: route, assign, layout, dispatch, stand-in, combine
     run_and_check(w, flags=flags, rep=rep, order=order, logits=logits, x=x)
+    # route, assign and layout as one call: equal to the separate calls
+    run_both(w, rep=rep, order=order, logits=logits)
     # single-send layout, dispatch and fan-out
     b, ss, expanded = run_single_send(w, logits, x, rep, flags)
     ref = oracle.route_and_layout(w.T, w.E, w.k, w.R, logits, rep, order)
