@@ -170,6 +170,30 @@ int moe_c_abi_check(void) {
     const int ea = h_idx[a], eb = h_idx[b];
     if (ea > eb || (ea == eb && a > b)) FAIL("send rows %d, %d out of (expert, token) order", r - 1, r);
   }
+  /* the one-call route + assignment + layout writes the same tables */
+  {
+    int32_t* h_pos2 = (int32_t*)malloc(4u * n);
+    int32_t* h_idx2 = (int32_t*)malloc(4u * n);
+    int32_t* h_roff2 = (int32_t*)malloc(4u * (R + 1));
+    int same = h_pos2 && h_idx2 && h_roff2;
+    if (same) {
+      HIP_OK(hipMemset(d_pos, 0xff, 4u * n));
+      MOE_OK_OR_FAIL(moe_route_assign_layout(&p, (const float*)d_logits, NULL, 1, (int32_t*)d_idx,
+                                             (float*)d_w, (int32_t*)d_counts, (int32_t*)d_assign,
+                                             (int32_t*)d_active, (int32_t*)d_rank_of,
+                                             (int32_t*)d_eoff, (int32_t*)d_roff, (int32_t*)d_pos,
+                                             (int32_t*)d_src, (int32_t*)d_dedup, d_ws, ws_bytes,
+                                             NULL));
+      HIP_OK(hipDeviceSynchronize());
+      HIP_OK(hipMemcpy(h_pos2, d_pos, 4u * n, hipMemcpyDeviceToHost));
+      HIP_OK(hipMemcpy(h_idx2, d_idx, 4u * n, hipMemcpyDeviceToHost));
+      HIP_OK(hipMemcpy(h_roff2, d_roff, 4u * (R + 1), hipMemcpyDeviceToHost));
+      same = memcmp(h_pos2, h_pos, 4u * n) == 0 && memcmp(h_idx2, h_idx, 4u * n) == 0 &&
+             memcmp(h_roff2, h_roff, 4u * (R + 1)) == 0;
+    }
+    free(h_pos2); free(h_idx2); free(h_roff2);
+    if (!same) FAIL("moe_route_assign_layout differs from the three calls");
+  }
   printf("c-abi check ok: T=%d E=%d k=%d H=%d R=%d\n", T, E, K, H, R);
 
 done:
