@@ -27,7 +27,8 @@
 //     ids with one ballot per id bit and counting lower lanes; across the
 //     block's waves by per-wave counts in LDS; across rounds by running
 //     per-expert cursors. pos = cursor + rank, src[pos] = flat pair index.
-//  (4. layout_single_send, for the single-send rows.)
+//  (3'. layout_permute_ss: the permutation and then the single-send rows,
+//   in one launch, when the single-send rows are asked for.)
 // A small batch (T k <= 8192 pairs) runs all of it in one workgroup instead
 // (layout_small), sharing the same device functions.
 #include "device.hpp"
@@ -400,27 +401,45 @@ __device__ __forceinline__ void single_send_rounds(const int32_t* __restrict__ i
   }
 }
 
+// The permutation and the single-send rows of one block of tokens in one
+// launch: the permutation rounds of layout_permute_kernel, then the
+// single-send rounds, the second reusing the first's LDS tables.
+// LDS: max((1 + 2 WAVES) E, E + (1 + 2 WAVES) R) ints.
 template <int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void layout_single_send_kernel(
+__global__ __launch_bounds__(WAVES * kWave) void layout_permute_ss_kernel(
     const int32_t* __restrict__ idx, int T, int E, int k, int R, int tpb,
-    const int32_t* __restrict__ rank_of, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ expert_offsets,
+    const int32_t* __restrict__ rank_of, const int32_t* __restrict__ ss_base,
     const int32_t* __restrict__ ss_rank_offsets, const int32_t* __restrict__ lead_mask,
-    int32_t* __restrict__ ss_row, int32_t* __restrict__ ss_token) {
+    int32_t* __restrict__ pos, int32_t* __restrict__ src, int32_t* __restrict__ ss_row,
+    int32_t* __restrict__ ss_token) {
   extern __shared__ int smem[];
+  const int b = blockIdx.x;
+  const int64_t i0 = (int64_t)b * tpb * k;
+  const int64_t i1 = min((int64_t)T * k, i0 + (int64_t)tpb * k);
+  {
+    int* run = smem;                   // [E] next free row of each expert
+    int* wcnt = smem + E;              // [WAVES][E]
+    int* wtag = smem + E + WAVES * E;  // [WAVES][E]
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      run[e] = expert_offsets[e] + base[(size_t)b * E + e];
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) wtag[w * E + e] = 0;
+    }
+    __syncthreads();
+    permute_rounds<WAVES>(idx, i0, i1, E, T * k, run, wcnt, wtag, pos, src);  // ends with a barrier
+  }
   int* s_rank = smem;                       // [E]
   int* run = smem + E;                      // [R] next free single-send row of each rank
-  int* wcnt = smem + E + R;                 // [WAVES][R] leaders per rank in a wave
-  int* wtag = smem + E + R + WAVES * R;     // [WAVES][R] round that wrote wcnt
-  const int b = blockIdx.x;
+  int* wcnt = smem + E + R;                 // [WAVES][R]
+  int* wtag = smem + E + R + WAVES * R;     // [WAVES][R]
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_rank[e] = rank_of[e];
   for (int r = threadIdx.x; r < R; r += blockDim.x) {
-    run[r] = ss_rank_offsets[r] + base[(size_t)b * R + r];
+    run[r] = ss_rank_offsets[r] + ss_base[(size_t)b * R + r];
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) wtag[w * R + r] = 0;
   }
   __syncthreads();
-  const int64_t i0 = (int64_t)b * tpb * k;
-  const int64_t i1 = min((int64_t)T * k, i0 + (int64_t)tpb * k);
   single_send_rounds<WAVES>(idx, i0, i1, k, E, R, T * k, s_rank, run, wcnt, wtag, lead_mask,
                             ss_row, ss_token);
 }
@@ -591,6 +610,23 @@ hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const i
                                                ss_rank_offsets);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
+  if (ss) {
+    // permutation and single-send rows in one launch; 16 waves when blocks
+    // hold many pairs and both phases' tables stay small
+    const bool w16 = (int64_t)bl.layout_tpb * k >= 1024 && E <= 256 && E + 33 * R <= 12 * 1024;
+    const int W = w16 ? 16 : 4;
+    const size_t pe = (size_t)(1 + 2 * W) * E, pr = (size_t)E + (size_t)(1 + 2 * W) * R;
+    const size_t lds = (pe > pr ? pe : pr) * sizeof(int);
+    if (w16)
+      layout_permute_ss_kernel<16><<<nblk, 16 * kWave, lds, s>>>(
+          idx, T, E, k, R, bl.layout_tpb, hist, expert_offsets, rank_of, ded, ss_rank_offsets,
+          lead, pos, src, ss_row, ss_token);
+    else
+      layout_permute_ss_kernel<4><<<nblk, 4 * kWave, lds, s>>>(
+          idx, T, E, k, R, bl.layout_tpb, hist, expert_offsets, rank_of, ded, ss_rank_offsets,
+          lead, pos, src, ss_row, ss_token);
+    return hipGetLastError();
+  }
   // 16 waves per permute block when blocks hold many pairs and the per-wave
   // LDS tables (33 E ints) fit comfortably; else 4 waves (9 E ints)
   if (E <= 256 && (int64_t)bl.layout_tpb * k >= 1024)
@@ -599,15 +635,6 @@ hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const i
   else
     layout_permute_kernel<4><<<nblk, 4 * kWave, 9 * E * sizeof(int), s>>>(
         idx, T, E, k, bl.layout_tpb, hist, expert_offsets, pos, src);
-  err = hipGetLastError();
-  if (err != hipSuccess || !ss) return err;
-  // LDS: E + (1 + 2 WAVES) R ints; 16 waves while that stays small
-  if ((int64_t)bl.layout_tpb * k >= 1024 && E + 33 * R <= 12 * 1024)
-    layout_single_send_kernel<16><<<nblk, 16 * kWave, (E + 33 * R) * sizeof(int), s>>>(
-        idx, T, E, k, R, bl.layout_tpb, rank_of, ded, ss_rank_offsets, lead, ss_row, ss_token);
-  else
-    layout_single_send_kernel<4><<<nblk, 4 * kWave, (E + 9 * R) * sizeof(int), s>>>(
-        idx, T, E, k, R, bl.layout_tpb, rank_of, ded, ss_rank_offsets, lead, ss_row, ss_token);
   return hipGetLastError();
 }
 
