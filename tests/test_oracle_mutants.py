@@ -80,6 +80,23 @@ def greedy_ties_to_higher_gpu(counts, R, rep, order="constrained"):
     return np.where(a >= 0, R - 1 - a, a).astype(a.dtype), act[::-1].copy()
 
 
+def greedy_ties_to_first_listed_replica(counts, R, rep, order="constrained"):
+    """Fewest activated experts, ties to the earlier replica slot rather than
+    the lower GPU index."""
+    counts = np.asarray(counts)
+    E = counts.shape[0]
+    cand = oracle.candidates(E, R, rep)
+    live = [e for e in range(E) if counts[e] > 0]
+    if order == "constrained":
+        live.sort(key=lambda e: (len(cand[e]), e))
+    active, assign = [0] * R, [-1] * E
+    for e in live:
+        slot = min(range(len(cand[e])), key=lambda s: (active[cand[e][s]], s))
+        assign[e] = cand[e][slot]
+        active[assign[e]] += 1
+    return np.array(assign, dtype=np.int32), np.array(active, dtype=np.int32)
+
+
 def greedy_always_id_order(counts, R, rep, order="constrained"):
     return O["greedy_assign"](counts, R, rep, "id")
 
@@ -167,6 +184,11 @@ CASES = [
     ("greedy ties to the higher GPU", "greedy_assign", greedy_ties_to_higher_gpu,
      [(TP.test_handworked_replicated_instances, ()),
       (TP.test_decode_table_all_active_closed_form, ("id", "active_id_order"))]),
+    ("greedy ties to the first-listed replica", "greedy_assign", greedy_ties_to_first_listed_replica,
+     [(TP.test_decode_table_all_active_full_assignment, ("constrained", "two_copy_assign_constrained_order")),
+      (TP.test_handworked_ties_go_to_the_lower_gpu_not_the_first_slot, ()),
+      (TP.test_greedy_matches_scan_reimplementation_on_shuffled_slots, (0,)),
+      (TP.test_greedy_does_not_depend_on_replica_slot_order, (0,))]),
     ("greedy ignores the most-constrained order", "greedy_assign", greedy_always_id_order,
      [(TP.test_decode_table_all_active_closed_form, ("constrained", "active_constrained_order"))]),
     ("tokens descending inside an expert", "permutation", permutation_tokens_descending,

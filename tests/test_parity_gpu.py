@@ -213,3 +213,32 @@ def test_two_streams_concurrently():
             for k, v in wnt.items():
                 got = getattr(b, k)
                 assert torch.equal(got.contiguous().view(torch.uint8), v.contiguous().view(torch.uint8)), k
+
+
+@pytest.mark.parametrize("reverse", [False, True], ids=["listed", "slots_reversed"])
+@pytest.mark.parametrize("order", ["constrained", "id"])
+def test_decode_table_all_active_full_assignment(order, reverse):
+    """The assignment kernel on the all-active decode table against the
+    hand-derived assignment of every expert (ties to the lower GPU index,
+    whatever the order of the replica slots)."""
+    from conftest import load_golden
+    g = load_golden("decode_replica_closed_form.json")
+    key = "two_copy_assign_constrained_order" if order == "constrained" else "two_copy_assign_id_order"
+    two = {int(e): gpu for e, gpu in g[key].items()}
+    expected = [two.get(e, e // 32) for e in range(256)]
+    rep = synth.replica_table(synth.DECODE)
+    if reverse:
+        rep = np.where(rep[:, 1:2] >= 0, rep[:, ::-1], rep).astype(np.int32)
+    say(f"[case] decode all-active assignment order={order} reversed={reverse}")
+    w = synth.DECODE
+    flags = B.MOE_FLAG_GREEDY_ID_ORDER if order == "id" else 0
+    p = B.make_problem(w.T, w.E, w.k, w.H, w.R, w.act_dtype, flags)
+    dev = torch.device("cuda")
+    counts = torch.ones(w.E, dtype=torch.int32, device=dev)
+    rep_t = torch.from_numpy(np.ascontiguousarray(rep)).to(dev)
+    assign = torch.empty(w.E, dtype=torch.int32, device=dev)
+    active = torch.empty(w.R, dtype=torch.int32, device=dev)
+    B.moe_assign_replicas(p, counts, rep_t, rep.shape[1], assign, active)
+    torch.cuda.synchronize()
+    assert assign.cpu().tolist() == expected
+    assert active.cpu().tolist() == g["active_constrained_order" if order == "constrained" else "active_id_order"]
