@@ -597,6 +597,7 @@ def main():
         "max_active_experts": int(b.active.max().item()),
         "copy_reference_GBps": round(copy_gbps, 1),
         "fill_reference_GBps": None if fill_gbps is None else round(fill_gbps, 1),
+        "build_id": B.moe_build_id(),
         "inputs": {"numpy": np.__version__,
                    "logits_sha256": hashlib.sha256(logits.tobytes()).hexdigest()[:16],
                    "x_sha256": hashlib.sha256(x.tobytes()).hexdigest()[:16]},

@@ -6,7 +6,9 @@ pointers, the stream becomes torch's current HIP stream unless given, and
 tensor sizes are checked against the problem so the library can never be
 handed a buffer shorter than the shape it is told about. Every step of the
 routing path runs in the HIP library; there is no fallback. If the library is
-missing, importing this module raises.
+missing, or was built from sources other than those beside it (its
+moe_build_id() differs from the digest of csrc/ and include/), importing this
+module raises.
 """
 from __future__ import annotations
 
@@ -14,6 +16,8 @@ import ctypes
 import os
 
 import torch
+
+from . import build as _build
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_route.so")
 
@@ -24,7 +28,7 @@ MOE_FLAG_OUT_F32 = 1 << 1
 MOE_MAX_E, MOE_MAX_K, MOE_MAX_R, MOE_MAX_REP = 1024, 16, 1024, 16
 MOE_MAX_ROWS = (1 << 24) - 1
 
-EXPORTED = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
+EXPORTED = ("moe_version", "moe_build_id", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
             "moe_route", "moe_assign_replicas", "moe_layout", "moe_route_assign_layout",
             "moe_layout_single_send",
             "moe_single_send_dispatch", "moe_single_send_expand", "moe_dispatch",
@@ -58,6 +62,7 @@ def _load() -> ctypes.CDLL:
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     sig = {
         "moe_version": (i32, []),
+        "moe_build_id": (ctypes.c_char_p, []),
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_workspace_bytes": (i32, [P, ctypes.POINTER(sz)]),
@@ -81,6 +86,10 @@ def _load() -> ctypes.CDLL:
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
         f.restype, f.argtypes = res, args
+    built, want = lib.moe_build_id().decode(), _build.source_digest()
+    if built != want:
+        raise ImportError(f"{LIB_PATH} was built from other sources (build id {built}, sources "
+                          f"{want}); rebuild with `python combine_router_topk_amd/build.py`")
     return lib
 
 
@@ -137,6 +146,10 @@ def _stream(stream) -> ctypes.c_void_p:
 
 def moe_version() -> int:
     return _lib.moe_version()
+
+
+def moe_build_id() -> str:
+    return _lib.moe_build_id().decode()
 
 
 def moe_status_string(status: int) -> str:

@@ -8,6 +8,7 @@ imports nothing from the package.
 from __future__ import annotations
 
 import glob
+import hashlib
 import os
 import subprocess
 from concurrent.futures import ThreadPoolExecutor
@@ -21,12 +22,33 @@ LIB = os.path.join(PKG, "libmoe_route.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-CFLAGS = [
+CFLAGS_BASE = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}",
+    "-Wall", "-Wno-unused-function",
 ]
+CFLAGS = CFLAGS_BASE + [f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def source_files() -> list[str]:
+    """Every file the library is compiled from: the HIP sources and headers
+    under csrc/ and the public header."""
+    pats = [os.path.join(CSRC, "*.hip"), os.path.join(CSRC, "*.hpp"), os.path.join(INCLUDE, "*.h")]
+    return sorted(f for p in pats for f in glob.glob(p))
+
+
+def source_digest() -> str:
+    """Build id: the first 16 hex digits of a SHA-256 over the compile flags
+    and, in path order, each source file's path (relative to the repository)
+    and bytes. The library returns the id it was built with from
+    moe_build_id(), so a loader can tell a library built from other sources."""
+    h = hashlib.sha256(" ".join(CFLAGS_BASE).encode())
+    for f in source_files():
+        h.update(b"\0" + os.path.relpath(f, ROOT).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def _run(cmd: list[str]) -> None:
@@ -42,8 +64,9 @@ def build(jobs: int = 8) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    bid = f'-DMOE_BUILD_ID="{source_digest()}"'
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        list(ex.map(lambda so: _run([HIPCC, *CFLAGS, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
+        list(ex.map(lambda so: _run([HIPCC, *CFLAGS, bid, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)

@@ -7,6 +7,12 @@
 #include "launch.hpp"
 #include "moe_route.h"
 
+// Set by the build to a digest of the sources and flags; a library compiled
+// any other way reports "unknown", which no loader accepts.
+#ifndef MOE_BUILD_ID
+#define MOE_BUILD_ID "unknown"
+#endif
+
 namespace {
 
 thread_local char g_last_error[256] = "";
@@ -75,7 +81,9 @@ moe_status check_rep(const moe_problem* p, const int32_t* rep, int32_t maxrep, c
 
 extern "C" {
 
-int32_t moe_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int32_t moe_version(void) { return 1 * 10000 + 1 * 100 + 0; }
+
+const char* moe_build_id(void) { return MOE_BUILD_ID; }
 
 const char* moe_status_string(int32_t status) {
   switch (status) {

@@ -96,6 +96,13 @@ typedef struct {
 /* Version of this ABI (major * 10000 + minor * 100 + patch). */
 int32_t moe_version(void);
 
+/* Identity of the build: 16 hex digits of a SHA-256 over the compile flags
+ * and the bytes of every source and header the library was compiled from
+ * ("unknown" when built without the package's build script). A loader
+ * compares it with the digest of the sources beside it to refuse a stale
+ * library. Static string; host only. */
+const char* moe_build_id(void);
+
 /* Static text for a status code ("unknown status" for other values). */
 const char* moe_status_string(int32_t status);
 

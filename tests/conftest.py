@@ -10,17 +10,34 @@ if ROOT not in sys.path:
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 LIB = os.path.join(ROOT, "combine_router_topk_amd", "libmoe_route.so")
 
-# Tests load what is built; they build only when nothing is.
+# Tests load what is built; they build only when nothing is. A library built
+# from other sources than those in the tree is refused, never run.
 C_CHECK_LIB = os.path.join(ROOT, "tests", "c_abi", "libcheck_abi.so")
-if not os.path.exists(LIB) or not os.path.exists(C_CHECK_LIB):
+
+
+def _build_module():
     import importlib.util
-    _spec = importlib.util.spec_from_file_location(
+    spec = importlib.util.spec_from_file_location(
         "_moe_build", os.path.join(ROOT, "combine_router_topk_amd", "build.py"))
-    _mod = importlib.util.module_from_spec(_spec)
-    _spec.loader.exec_module(_mod)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+_BUILD = _build_module()
+if not os.path.exists(LIB) or not os.path.exists(C_CHECK_LIB):
     if not os.path.exists(LIB):
-        _mod.build()
-    _mod.build_c_check()
+        _BUILD.build()
+    _BUILD.build_c_check()
+import ctypes as _ct  # noqa: E402
+
+_id_fn = _ct.CDLL(LIB).moe_build_id
+_id_fn.restype = _ct.c_char_p
+BUILD_ID = _id_fn().decode()
+if BUILD_ID != _BUILD.source_digest():
+    raise RuntimeError(f"{LIB} is stale: built from sources with id {BUILD_ID}, the tree's sources "
+                       f"have id {_BUILD.source_digest()}; run `python combine_router_topk_amd/build.py`")
+print(f"libmoe_route.so build id {BUILD_ID}", flush=True)
 
 
 def pytest_configure(config):

@@ -27,6 +27,26 @@ def test_header_declares_and_library_exports_every_entry_point():
         assert hasattr(lib, n), n
 
 
+def test_build_id_is_the_digest_of_the_sources_and_a_mismatch_is_refused(monkeypatch):
+    from combine_router_topk_amd import build
+    bid = B.moe_build_id()
+    assert len(bid) == 16 and int(bid, 16) >= 0
+    assert bid == build.source_digest()
+    monkeypatch.setattr(build, "source_digest", lambda: "0" * 16)
+    with pytest.raises(ImportError, match="other sources"):
+        B._load()
+
+
+def test_source_digest_covers_every_source_and_header():
+    from combine_router_topk_amd import build
+    names = {os.path.relpath(f, ROOT) for f in build.source_files()}
+    assert "include/moe_route.h" in names
+    csrc = os.path.join(ROOT, "combine_router_topk_amd", "csrc")
+    for f in os.listdir(csrc):
+        if f.endswith((".hip", ".hpp")):
+            assert os.path.join("combine_router_topk_amd", "csrc", f) in names, f
+
+
 def test_version_and_status_strings():
     assert B.moe_version() >= 10000
     assert B.moe_status_string(0) == "ok"
