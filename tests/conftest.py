@@ -31,6 +31,11 @@ if not os.path.exists(LIB) or not os.path.exists(C_CHECK_LIB):
     _BUILD.build_c_check()
 import ctypes as _ct  # noqa: E402
 
+# torch first: it loads the HIP runtime it ships, and the library then binds
+# to that same runtime (same soname). Loading the library first would pull
+# in the system runtime under that name and torch would run on it.
+import torch  # noqa: E402,F401
+
 _id_fn = _ct.CDLL(LIB).moe_build_id
 _id_fn.restype = _ct.c_char_p
 BUILD_ID = _id_fn().decode()

@@ -8,6 +8,7 @@ bound k * 2^-24 * sum_j |w_j y_j| for the fp32 output.
 """
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -106,3 +107,77 @@ def check_rows(b: P.Buffers, ref: dict, x: np.ndarray, w: synth.Workload,
     else:
         bad = np.abs(got - refo) > OUT_ATOL + OUT_RTOL * np.abs(refo)
     assert not bad.any(), ("out", np.argwhere(bad)[:5], got[bad][:5], refo[bad][:5])
+
+
+# ---- full-size comparisons, every element ------------------------------------
+
+def token_chunks(T: int, k: int, H: int, max_elems: int = 1 << 26, min_chunks: int = 16):
+    """Token ranges [t0, t1) covering the batch, each small enough that one
+    chunk's rows (about k*H elements per token) stay a few hundred MB on the
+    host, and at least min_chunks of them so the thread pool has work."""
+    per = max(1, min(max_elems // max(1, k * H), -(-T // min_chunks)))
+    return [(t0, min(T, t0 + per)) for t0 in range(0, T, per)]
+
+
+def run_chunked(gather, check, chunks, workers: int = 16) -> None:
+    """gather(t0, t1) runs on the calling thread (device-to-host copies in
+    stream order) and returns host arrays; check(t0, t1, *arrays) runs the
+    oracle and the comparison on a thread pool (numpy releases the GIL in its
+    array loops). At most 2 * workers chunks are in flight; the first failure
+    is raised."""
+    from concurrent.futures import ThreadPoolExecutor
+    workers = max(1, min(workers, os.cpu_count() or 1))
+    pending = []
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for t0, t1 in chunks:
+            arrays = gather(t0, t1)
+            pending.append(ex.submit(check, t0, t1, *arrays))
+            if len(pending) >= 2 * workers:
+                pending.pop(0).result()
+        for f in pending:
+            f.result()
+
+
+def chunk_rows(ref: dict, k: int, t0: int, t1: int):
+    """The send rows of tokens [t0, t1) in (token, slot) order, and a pos table
+    into a compact array holding them in that order."""
+    items = np.arange(t0 * k, t1 * k)
+    rows = ref["pos"][items].astype(np.int64)
+    pos_c = np.zeros(ref["pos"].shape[0], dtype=np.int64)
+    pos_c[items] = np.arange(items.shape[0])
+    return rows, pos_c
+
+
+def oracle_y(ref: dict, x: np.ndarray, w: synth.Workload, rows: np.ndarray) -> np.ndarray:
+    """The oracle's stand-in rows for the given send rows, from their own
+    dispatch rows."""
+    flat = ref["idx"].ravel()
+    return oracle.expert_standin(oracle.dispatch_rows(x, ref["src"], w.k, rows),
+                                 flat[ref["src"][rows]], w.E, w.act_dtype)
+
+
+def check_rows_all(b: P.Buffers, ref: dict, x: np.ndarray, w: synth.Workload) -> None:
+    """Every stand-in row bit for bit and every combine output element within
+    1e-3 + 4e-3 |ref| against the oracle, token chunk by token chunk (each
+    chunk's k T_c send rows and T_c output rows)."""
+    k = w.k
+
+    def gather(t0, t1):
+        rows, _ = chunk_rows(ref, k, t0, t1)
+        rt = torch.from_numpy(rows).to(b.y.device)
+        return (tensor_bits(b.y.index_select(0, rt)),
+                b.out[t0:t1].float().cpu().numpy())
+
+    def check(t0, t1, got_y, got_out):
+        rows, pos_c = chunk_rows(ref, k, t0, t1)
+        y_ref = oracle_y(ref, x, w, rows)
+        if not np.array_equal(got_y, y_ref):
+            bad = np.argwhere(got_y != y_ref)[:6]
+            raise AssertionError(f"y rows of tokens [{t0}, {t1}): {int((got_y != y_ref).sum())} "
+                                 f"mismatches at (send row, col) {[(int(rows[i]), int(c)) for i, c in bad]}")
+        out_ref = oracle.combine(y_ref, pos_c, ref["w"], k, w.act_dtype, np.arange(t0, t1))
+        got = got_out.astype(np.float64)
+        bad = np.abs(got - out_ref) > OUT_ATOL + OUT_RTOL * np.abs(out_ref)
+        assert not bad.any(), ("out", t0, np.argwhere(bad)[:5], got[bad][:5], out_ref[bad][:5])
+
+    run_chunked(gather, check, token_chunks(w.T, k, w.H))
