@@ -445,10 +445,36 @@ def graph_leg(P, B, synth, np, torch, dev, steps, seed):
                            "graph_us_per_step": round(fused_graph_us, 1)}}
 
 
+def separate_calls_leg(P, b, flush, steps, ev, np, torch) -> dict:
+    """Route, assignment and layout as three separate calls (the kernels of
+    moe_route, moe_assign_replicas and moe_layout), each bracketed by events,
+    for comparison with the one-call plan the headline step uses. A fill of
+    the flush buffer first keeps the GPU busy while the host enqueues them,
+    as in the headline step, so the brackets hold kernel time, not launch
+    latency."""
+    marks = []
+    for i in range(steps + 2):
+        if flush is not None:
+            flush.fill_(8.0)
+        e = [ev() for _ in range(4)]
+        e[0].record()
+        P.route(b)
+        e[1].record()
+        P.assign(b)
+        e[2].record()
+        P.layout(b)
+        e[3].record()
+        if i >= 2:
+            marks.append(e)
+    torch.cuda.synchronize()
+    return {name: round(float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks])), 4)
+            for i, name in enumerate(("route", "assign", "layout"))}
+
+
 def path_summary(w, meta_ms: dict, disp_ms: float, comb_ms: float, dc_bytes: int) -> dict:
-    """The whole forward path (route, assign, layout, dispatch, combine; the
-    expert stand-in and the cache flushes excluded), kernel time summed per
-    stage. Algorithmic bytes: dispatch and combine rows, the logits, and 32
+    """The whole forward path (the one-call route + assignment + layout, then
+    dispatch and combine; the expert stand-in and the cache flushes excluded),
+    kernel time summed per stage. Algorithmic bytes: dispatch and combine rows, the logits, and 32
     bytes of metadata per (token, slot) pair (route writes idx and w; layout
     reads idx and writes pos and src; dispatch reads pos; combine reads pos
     and w)."""
@@ -492,14 +518,10 @@ def main():
     marks, meta_marks = [], []
 
     def step(record: bool):
-        m0, m1, m2, m3 = ev(), ev(), ev(), ev()
+        m0, m1 = ev(), ev()
         m0.record()
-        P.route(b)
+        P.route_assign_layout(b)
         m1.record()
-        P.assign(b)
-        m2.record()
-        P.layout(b)
-        m3.record()
         if flush is not None:
             flush.fill_(1.0)
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
@@ -514,7 +536,7 @@ def main():
         e3.record()
         if record:
             marks.append((e0, e1, e2, e3))
-            meta_marks.append((m0, m1, m2, m3))
+            meta_marks.append((m0, m1))
 
     for _ in range(args.warmup):
         step(False)
@@ -525,8 +547,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    meta_ms = {name: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in meta_marks]))
-               for i, name in enumerate(("route", "assign", "layout"))}
+    meta_ms = {"plan": float(np.mean([a.elapsed_time(c) for a, c in meta_marks]))}
     disp_all = [a.elapsed_time(b_) for a, b_, _, _ in marks]
     comb_all = [c.elapsed_time(d) for _, _, c, d in marks]
     disp_ms, comb_ms = float(np.mean(disp_all)), float(np.mean(comb_all))
@@ -590,6 +611,7 @@ def main():
         "path": path_summary(w, meta_ms, disp_ms, comb_ms, dc_bytes),
         "stage_ms": {**{k_: round(v_, 4) for k_, v_ in meta_ms.items()},
                      "dispatch": round(disp_ms, 4), "combine": round(comb_ms, 4)},
+        "separate_calls_ms": separate_calls_leg(P, b, flush, 20, ev, np, torch),
         "median_ms": {"dispatch": round(float(np.median(disp_all)), 4),
                       "combine": round(float(np.median(comb_all)), 4)},
         "dedup_rows": int(b.dedup.sum().item()),

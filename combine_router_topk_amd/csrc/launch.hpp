@@ -37,8 +37,11 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
 
 // The top-k kernel of launch_route alone: idx, w, and one histogram row per
 // route block in ws ([blocking_for(T, E, R).route_nblk, E]), no counts.
+// With ded_rows (R | E, contiguous partition), also one row per route block
+// of per-rank token counts ([route_nblk, R]: tokens of the block with at
+// least one selected expert on the rank).
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
-                             int32_t* ws, hipStream_t s);
+                             int32_t* ws, hipStream_t s, int32_t* ded_rows = nullptr, int R = 1);
 
 // route, assign and layout of one batch: for a small batch the top-k kernel
 // and one workgroup that does everything else, else the three launches.

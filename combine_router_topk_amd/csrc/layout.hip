@@ -576,6 +576,140 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_small_kernel(
                      pos, src, dedup, nullptr, nullptr, nullptr, nullptr, region, s_wave, s_wave2);
 }
 
+// The one-call plan of a batch without a replica table (contiguous
+// partition: expert e on rank e / per), after a top-k kernel that wrote one
+// expert-histogram row and one per-rank count row per route block. There is
+// no choice to make, and the send order (rank, expert) is expert order, so
+// the plan is two launches: this column scan, then the permutation with the
+// expert-offset scan in its prologue.
+//
+// One workgroup per task of 64 columns: the expert tasks replace their
+// columns of the histogram rows with exclusive prefixes over blocks (the
+// block's first row per expert) and write the totals as counts, with
+// rank_of and assign; the rank tasks sum their columns into dedup. The 16
+// waves split the rows (at most kSumRows each, so 512 route blocks) and load
+// their segment at once.
+constexpr int kSumRows = 32;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_scan_kernel(
+    int32_t* __restrict__ hist, const int32_t* __restrict__ ded, int nblk, int E, int R, int per,
+    int32_t* __restrict__ counts, int32_t* __restrict__ assign, int32_t* __restrict__ rank_of,
+    int32_t* __restrict__ dedup) {
+  __shared__ int part[kPlanWaves][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int ch_h = (E + kWave - 1) / kWave;
+  const bool is_h = static_cast<int>(blockIdx.x) < ch_h;
+  const int cols = is_h ? E : R;
+  const int c = (is_h ? blockIdx.x : blockIdx.x - ch_h) * kWave + lane;
+  const int32_t* M = is_h ? hist : ded;
+  const int seg = (nblk + kPlanWaves - 1) / kPlanWaves;
+  const int r_lo = min(nblk, wave * seg), r_hi = min(nblk, r_lo + seg);
+  int v[kSumRows];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kSumRows; ++i) {
+    const int r = r_lo + i;
+    v[i] = (c < cols && r < r_hi) ? M[(size_t)r * cols + c] : 0;
+    sum += v[i];
+  }
+  part[wave][lane] = sum;
+  __syncthreads();
+  int pre = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanWaves; ++i) {
+    const int x = part[i][lane];
+    pre += (i < wave) ? x : 0;
+    all += x;
+  }
+  if (c >= cols) return;
+  if (is_h) {
+    int run = pre;
+#pragma unroll
+    for (int i = 0; i < kSumRows; ++i) {
+      const int r = r_lo + i;
+      if (r < r_hi) hist[(size_t)r * E + c] = run;
+      run += v[i];
+    }
+    if (wave == 0) {
+      counts[c] = all;
+      rank_of[c] = c / per;
+      assign[c] = all > 0 ? c / per : -1;
+    }
+  } else if (wave == 0) {
+    dedup[c] = all;
+  }
+}
+
+// Permutation of one route block's pairs for a batch without a replica
+// table, after plan_scan_kernel. Prologue: the exclusive scan of counts over
+// experts (each thread a run of up to 4 consecutive experts, then a block
+// scan) gives expert_offsets; a block's cursors are those plus its
+// histogram prefix (base). Block 0 also writes expert_offsets, rank_offsets
+// (the offset of each rank's first expert; [R] = T k) and active (experts
+// with rows, per rank). Then the permutation rounds of layout_permute_kernel.
+// LDS: (1 + 2 WAVES) E + R ints.
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void layout_permute_scan_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int R, int per, int tpb,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ counts,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_offsets,
+    int32_t* __restrict__ active, int32_t* __restrict__ pos, int32_t* __restrict__ src) {
+  constexpr int kThreads = WAVES * kWave;
+  constexpr int kRun = (kMaxE + kThreads - 1) / kThreads;
+  extern __shared__ int smem[];
+  int* run = smem;                   // [E] next free row of each expert
+  int* wcnt = smem + E;              // [WAVES][E]
+  int* wtag = smem + E + WAVES * E;  // [WAVES][E]
+  int* s_act = wtag + WAVES * E;     // [R] (block 0)
+  __shared__ int s_wsum[WAVES];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int n_run = (E + kThreads - 1) / kThreads;
+  const int e0 = threadIdx.x * n_run;
+  int c[kRun], bs[kRun];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kRun; ++i) {
+    const int e = e0 + i;
+    const bool ok = i < n_run && e < E;
+    c[i] = ok ? counts[e] : 0;
+    bs[i] = ok ? base[(size_t)b * E + e] : 0;
+    sum += c[i];
+  }
+  for (int i = threadIdx.x; i < WAVES * E; i += kThreads) wtag[i] = 0;
+  if (b == 0)
+    for (int r = threadIdx.x; r < R; r += kThreads) s_act[r] = 0;
+  const int incl = wave_incl_scan(sum, lane);
+  if (lane == kWave - 1) s_wsum[wave] = incl;
+  __syncthreads();
+  int off = incl - sum;
+#pragma unroll
+  for (int i = 0; i < WAVES; ++i) off += (i < wave) ? s_wsum[i] : 0;
+#pragma unroll
+  for (int i = 0; i < kRun; ++i) {
+    const int e = e0 + i;
+    if (i < n_run && e < E) {
+      run[e] = off + bs[i];
+      if (b == 0) {
+        expert_offsets[e] = off;
+        if (e % per == 0) rank_offsets[e / per] = off;
+        if (c[i] > 0) atomicAdd(&s_act[e / per], 1);
+      }
+      off += c[i];
+    }
+  }
+  __syncthreads();
+  if (b == 0) {
+    for (int r = threadIdx.x; r < R; r += kThreads) active[r] = s_act[r];
+    if (threadIdx.x == 0) rank_offsets[R] = T * k;
+  }
+  const int64_t i0 = (int64_t)b * tpb * k;
+  const int64_t i1 = min((int64_t)T * k, i0 + (int64_t)tpb * k);
+  permute_rounds<WAVES>(idx, i0, i1, E, T * k, run, wcnt, wtag, pos, src);
+}
+
 }  // namespace
 
 hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const int32_t* assign,
@@ -652,6 +786,29 @@ hipError_t launch_route_assign_layout(const float* logits, int T, int E, int k, 
         ws, blocking_for(T, E, R).route_nblk, idx, T, E, k, R, rep, rep ? maxrep : 1,
         id_order ? 1 : 0, counts, assign, active, rank_of, expert_offsets, rank_offsets, pos, src,
         dedup);
+    return hipGetLastError();
+  }
+  if (rep == nullptr && T > 0) {
+    // no replica table: top-k with per-block counts, column scan, permutation
+    const Blocking bl = blocking_for(T, E, R);
+    const int nblk = bl.route_nblk, per = E / R;
+    int32_t* hist = ws;                          // [nblk, E]
+    int32_t* ded = ws + (size_t)nblk * E;        // [nblk, R]
+    hipError_t err = launch_route_topk(logits, T, E, k, idx, w, hist, s, ded, R);
+    if (err != hipSuccess) return err;
+    const int tasks = (E + kWave - 1) / kWave + (R + kWave - 1) / kWave;
+    plan_scan_kernel<<<tasks, kPlanThreads, 0, s>>>(hist, ded, nblk, E, R, per, counts, assign,
+                                                    rank_of, dedup);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (E <= 256 && (int64_t)bl.route_tpb * k >= 1024)
+      layout_permute_scan_kernel<16><<<nblk, 16 * kWave, (33 * E + R) * sizeof(int), s>>>(
+          idx, T, E, k, R, per, bl.route_tpb, hist, counts, expert_offsets, rank_offsets, active,
+          pos, src);
+    else
+      layout_permute_scan_kernel<4><<<nblk, 4 * kWave, (9 * E + R) * sizeof(int), s>>>(
+          idx, T, E, k, R, per, bl.route_tpb, hist, counts, expert_offsets, rank_offsets, active,
+          pos, src);
     return hipGetLastError();
   }
   hipError_t err = launch_route(logits, T, E, k, idx, w, counts, ws, s);

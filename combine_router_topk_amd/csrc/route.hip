@@ -30,12 +30,20 @@ namespace {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteTargetBlocks = 512;
 
+// With ded_rows set (contiguous partition, per = E / R experts per rank),
+// each block also counts, per rank, its tokens with at least one selected
+// expert on that rank (the single-send counts), written as one row of a
+// [blocks, R] matrix beside the expert histogram.
 template <int L, int V>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int tpb, int32_t* __restrict__ idx,
-    float* __restrict__ w, int32_t* __restrict__ block_hist) {
+    float* __restrict__ w, int32_t* __restrict__ block_hist, int32_t* __restrict__ ded_rows, int R,
+    int per) {
   extern __shared__ int s_hist[];
+  int* s_ded = s_hist + E;  // [R], used with ded_rows
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_hist[e] = 0;
+  if (ded_rows != nullptr)
+    for (int r = threadIdx.x; r < R; r += blockDim.x) s_ded[r] = 0;
   __syncthreads();
 
   constexpr int TPW = kWave / L;  // tokens per wave step
@@ -116,10 +124,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
       w[o] = static_cast<float>(ex / sum);
       atomicAdd(&s_hist[my_e], 1);
     }
+    if (ded_rows != nullptr) {  // uniform: a kernel argument
+      // a slot counts for its rank unless a lower slot of the token has it
+      const int rk = my_e / per;
+      bool dup = false;
+      for (int jj = 0; jj < k; ++jj) {
+        const int o = __shfl(rk, grp * L + jj, kWave);
+        dup |= (jj < sl) && (o == rk);
+      }
+      if (valid && sl < k && !dup) atomicAdd(&s_ded[rk], 1);
+    }
   }
   __syncthreads();
   int32_t* row = block_hist + (size_t)blockIdx.x * E;
   for (int e = threadIdx.x; e < E; e += blockDim.x) row[e] = s_hist[e];
+  if (ded_rows != nullptr) {
+    int32_t* drow = ded_rows + (size_t)blockIdx.x * R;
+    for (int r = threadIdx.x; r < R; r += blockDim.x) drow[r] = s_ded[r];
+  }
 }
 
 // One token per wave for wide rows (E > 128): lane l holds the V contiguous
@@ -134,12 +156,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 // rounded up to a power of two): token s of a batch keeps its slot j in lane
 // s KP + j, and one fp64 pass evaluates the whole batch. Evaluated per token,
 // the softmax used k of the 64 lanes for the cost of all.
+// ded_rows, R and per as in route_topk_kernel.
 template <int V, int KP>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_wave_kernel(
     const float* __restrict__ logits, int T, int E, int k, int tpb, int32_t* __restrict__ idx,
-    float* __restrict__ w, int32_t* __restrict__ block_hist) {
+    float* __restrict__ w, int32_t* __restrict__ block_hist, int32_t* __restrict__ ded_rows, int R,
+    int per) {
   extern __shared__ int s_hist[];
+  int* s_ded = s_hist + E;  // [R], used with ded_rows
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_hist[e] = 0;
+  if (ded_rows != nullptr)
+    for (int r = threadIdx.x; r < R; r += blockDim.x) s_ded[r] = 0;
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -183,6 +210,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_wave_kernel(
       idx[o] = static_cast<int32_t>(b_e);
       w[o] = static_cast<float>(ex / sum);
       atomicAdd(&s_hist[b_e], 1);
+    }
+    if (ded_rows != nullptr) {  // uniform: a kernel argument
+      // a slot counts for its rank unless a lower slot of the token has it
+      const int rk = static_cast<int>(b_e) / per;
+      bool dup = false;
+#pragma unroll
+      for (int jj = 0; jj < KP; ++jj) {
+        const int o = __shfl(rk, (lane & ~(KP - 1)) + jj, kWave);
+        dup |= (jj < j) && (o == rk);
+      }
+      if (on && !dup) atomicAdd(&s_ded[rk], 1);
     }
   };
 
@@ -228,6 +266,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_wave_kernel(
   __syncthreads();
   int32_t* row = block_hist + (size_t)blockIdx.x * E;
   for (int e = threadIdx.x; e < E; e += blockDim.x) row[e] = s_hist[e];
+  if (ded_rows != nullptr) {
+    int32_t* drow = ded_rows + (size_t)blockIdx.x * R;
+    for (int r = threadIdx.x; r < R; r += blockDim.x) drow[r] = s_ded[r];
+  }
 }
 
 // out[c] = sum over rows of M[rows, cols]; one block per 64 columns, the 16
@@ -261,22 +303,35 @@ __global__ __launch_bounds__(1024) void column_sum_kernel(const int32_t* __restr
   }
 }
 
+struct TopkArgs {
+  const float* logits;
+  int T, E, k, tpb, nblk;
+  int32_t* idx;
+  float* w;
+  int32_t* hist;
+  int32_t* ded;  // null: no per-rank counts
+  int R, per;
+  size_t lds() const { return (size_t)(E + (ded != nullptr ? R : 0)) * sizeof(int); }
+};
+
 template <int L, int V>
-hipError_t launch_topk(const float* logits, int T, int E, int k, int tpb, int nblk, int32_t* idx,
-                       float* w, int32_t* ws, hipStream_t s) {
-  route_topk_kernel<L, V><<<nblk, kRouteThreads, E * sizeof(int), s>>>(logits, T, E, k, tpb, idx, w, ws);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  route_topk_kernel<L, V><<<a.nblk, kRouteThreads, a.lds(), s>>>(a.logits, a.T, a.E, a.k, a.tpb, a.idx,
+                                                                 a.w, a.hist, a.ded, a.R, a.per);
   return hipGetLastError();
 }
 
 template <int V>
-hipError_t launch_wave(const float* logits, int T, int E, int k, int tpb, int nblk, int32_t* idx,
-                       float* w, int32_t* ws, hipStream_t s) {
-  const size_t lds = E * sizeof(int);
-  if (k <= 1) route_topk_wave_kernel<V, 1><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
-  else if (k <= 2) route_topk_wave_kernel<V, 2><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
-  else if (k <= 4) route_topk_wave_kernel<V, 4><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
-  else if (k <= 8) route_topk_wave_kernel<V, 8><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
-  else route_topk_wave_kernel<V, 16><<<nblk, kRouteThreads, lds, s>>>(logits, T, E, k, tpb, idx, w, ws);
+hipError_t launch_wave(const TopkArgs& a, hipStream_t s) {
+#define MOE_WAVE(KP)                                                                    \
+  route_topk_wave_kernel<V, KP><<<a.nblk, kRouteThreads, a.lds(), s>>>(                 \
+      a.logits, a.T, a.E, a.k, a.tpb, a.idx, a.w, a.hist, a.ded, a.R, a.per)
+  if (a.k <= 1) MOE_WAVE(1);
+  else if (a.k <= 2) MOE_WAVE(2);
+  else if (a.k <= 4) MOE_WAVE(4);
+  else if (a.k <= 8) MOE_WAVE(8);
+  else MOE_WAVE(16);
+#undef MOE_WAVE
   return hipGetLastError();
 }
 
@@ -316,7 +371,9 @@ Blocking blocking_for(int T, int E, int R) {
 
 size_t workspace_bytes(int T, int E, int R) {
   const Blocking b = blocking_for(T, E, R);
-  const size_t route = (size_t)b.route_nblk * E * sizeof(int32_t);
+  // route rows [blocks, E], plus [blocks, R] of per-rank counts when the
+  // one-call plan takes them from the top-k kernel
+  const size_t route = (size_t)b.route_nblk * (E + R) * sizeof(int32_t);
   const size_t layout = ((size_t)b.layout_nblk * (E + R) + (size_t)T) * sizeof(int32_t);
   size_t n = route > layout ? route : layout;
   n = (n + 255) & ~(size_t)255;
@@ -324,19 +381,20 @@ size_t workspace_bytes(int T, int E, int R) {
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
-                             int32_t* ws, hipStream_t s) {
+                             int32_t* ws, hipStream_t s, int32_t* ded_rows, int R) {
   if (T == 0) return hipSuccess;
   const Blocking b = blocking_for(T, E, 1);
   const int L = lanes_per_token(E);
   const int V = (E + L - 1) / L;  // L = 16: 1..4; 32: 3..4; 64: 3..16
-  const int tpb = b.route_tpb, n = b.route_nblk;
-  if (L == 16 && V == 1) return launch_topk<16, 1>(logits, T, E, k, tpb, n, idx, w, ws, s);
-  if (L == 16 && V == 2) return launch_topk<16, 2>(logits, T, E, k, tpb, n, idx, w, ws, s);
-  if (L == 16) return launch_topk<16, 4>(logits, T, E, k, tpb, n, idx, w, ws, s);
-  if (L == 32) return launch_topk<32, 4>(logits, T, E, k, tpb, n, idx, w, ws, s);
-  if (V <= 4) return launch_wave<4>(logits, T, E, k, tpb, n, idx, w, ws, s);
-  if (V <= 8) return launch_wave<8>(logits, T, E, k, tpb, n, idx, w, ws, s);
-  return launch_wave<16>(logits, T, E, k, tpb, n, idx, w, ws, s);
+  const TopkArgs a{logits, T, E, k, b.route_tpb, b.route_nblk, idx, w, ws, ded_rows, R,
+                   ded_rows != nullptr ? E / R : 1};
+  if (L == 16 && V == 1) return launch_topk<16, 1>(a, s);
+  if (L == 16 && V == 2) return launch_topk<16, 2>(a, s);
+  if (L == 16) return launch_topk<16, 4>(a, s);
+  if (L == 32) return launch_topk<32, 4>(a, s);
+  if (V <= 4) return launch_wave<4>(a, s);
+  if (V <= 8) return launch_wave<8>(a, s);
+  return launch_wave<16>(a, s);
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,

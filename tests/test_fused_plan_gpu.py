@@ -65,11 +65,16 @@ def test_small_batches_without_table(w):
     run_both(w, 1)
 
 
-# Larger batches run the three calls' kernels under the one call.
-@pytest.mark.parametrize("w", [synth.TRAIN_TOP2, synth.TRAIN_TOP6,
+# Larger batches without a replica table take three launches (top-k with
+# per-block counts, a column scan, the permutation with the offset scan);
+# with a table, the three calls' kernels under the one call.
+@pytest.mark.parametrize("w", [synth.TRAIN_TOP2, synth.TRAIN_TOP6, synth.LARGE,
+                               synth.scaled(synth.LARGE, T=20000),
                                synth.scaled(synth.TRAIN_TOP2, T=9001),
                                synth.Workload("E48_k5_R12", 12000, 48, 5, 8, 12, synth.BF16, "zipf1.2", False),
-                               synth.Workload("E64_k16_R64", 20000, 64, 16, 8, 64, synth.BF16, "zipf1.2", False)],
+                               synth.Workload("E64_k16_R64", 20000, 64, 16, 8, 64, synth.BF16, "zipf1.2", False),
+                               synth.Workload("E1024_R2_per512", 9000, 1024, 3, 8, 2, synth.BF16, "zipf1.2", False),
+                               synth.Workload("E96_R96_T1M", 1 << 20, 96, 1, 8, 96, synth.BF16, "none", False)],
                          ids=lambda w: w.name)
 def test_larger_batches(w):
     run_both(w, 2)
