@@ -4,8 +4,18 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 #include "moe_route.h"
+
+// Scratch of moe_route_assign_layout_noalloc: a static device array, so the
+// call needs no allocation. Each GPU the library runs on holds its own copy
+// for the life of the process. In host code `scratch` names a host-side
+// stand-in, never the device memory: kernels are given the device address
+// that hipGetSymbolAddress returns for the current device (static_scratch
+// below).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 // Set by the build to a digest of the sources and flags; a library compiled
 // any other way reports "unknown", which no loader accepts.
@@ -77,6 +87,57 @@ moe_status check_rep(const moe_problem* p, const int32_t* rep, int32_t maxrep, c
     if (_st != MOE_OK) return _st;      \
   } while (0)
 
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current) and kept.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status static_scratch(void** out, const char* fn) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_status(err, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return hip_status(err, fn);
+    if (ptr == nullptr) return fail(MOE_ERR_HIP, "%s: no device address for the static scratch", fn);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// Argument checks shared by the two route + assignment + layout calls.
+moe_status check_route_assign_layout(const moe_problem* p, const float* logits, const int32_t* rep,
+                                     int32_t maxrep, const int32_t* idx, const float* w,
+                                     const int32_t* counts, const int32_t* assign,
+                                     const int32_t* active, const int32_t* rank_of,
+                                     const int32_t* expert_offsets, const int32_t* rank_offsets,
+                                     const int32_t* pos, const int32_t* src, const int32_t* dedup,
+                                     const char* fn) {
+  CHECK(check_problem(p, fn));
+  CHECK(check_rep(p, rep, maxrep, fn));
+  CHECK(need(counts, 4, fn, "counts"));
+  CHECK(need(assign, 4, fn, "assign"));
+  CHECK(need(active, 4, fn, "active"));
+  CHECK(need(rank_of, 4, fn, "rank_of"));
+  CHECK(need(expert_offsets, 4, fn, "expert_offsets"));
+  CHECK(need(rank_offsets, 4, fn, "rank_offsets"));
+  CHECK(need(dedup, 4, fn, "dedup"));
+  if (p->T > 0) {
+    CHECK(need(logits, 4, fn, "logits"));
+    CHECK(need(idx, 4, fn, "idx"));
+    CHECK(need(w, 4, fn, "w"));
+    CHECK(need(pos, 4, fn, "pos"));
+    CHECK(need(src, 4, fn, "src"));
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -146,25 +207,36 @@ moe_status moe_route_assign_layout(const moe_problem* p, const float* logits, co
                                    int32_t* src, int32_t* dedup, void* ws, size_t ws_bytes,
                                    void* stream) {
   const char* fn = "moe_route_assign_layout";
-  CHECK(check_problem(p, fn));
-  CHECK(check_rep(p, rep, maxrep, fn));
-  CHECK(need(counts, 4, fn, "counts"));
-  CHECK(need(assign, 4, fn, "assign"));
-  CHECK(need(active, 4, fn, "active"));
-  CHECK(need(rank_of, 4, fn, "rank_of"));
-  CHECK(need(expert_offsets, 4, fn, "expert_offsets"));
-  CHECK(need(rank_offsets, 4, fn, "rank_offsets"));
-  CHECK(need(dedup, 4, fn, "dedup"));
+  CHECK(check_route_assign_layout(p, logits, rep, maxrep, idx, w, counts, assign, active, rank_of,
+                                  expert_offsets, rank_offsets, pos, src, dedup, fn));
   CHECK(need(ws, 256, fn, "ws"));
-  if (p->T > 0) {
-    CHECK(need(logits, 4, fn, "logits"));
-    CHECK(need(idx, 4, fn, "idx"));
-    CHECK(need(w, 4, fn, "w"));
-    CHECK(need(pos, 4, fn, "pos"));
-    CHECK(need(src, 4, fn, "src"));
-  }
   const size_t req = moe::workspace_bytes(p->T, p->E, p->R);
   if (ws_bytes < req) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, req);
+  clear_stale_error();
+  return hip_status(moe::launch_route_assign_layout(
+                        logits, p->T, p->E, p->k, p->R, rep, maxrep,
+                        (p->flags & MOE_FLAG_GREEDY_ID_ORDER) != 0, idx, w, counts, assign, active,
+                        rank_of, expert_offsets, rank_offsets, pos, src, dedup,
+                        static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+moe_status moe_route_assign_layout_noalloc(const moe_problem* p, const float* logits,
+                                           const int32_t* rep, int32_t maxrep, int32_t* idx,
+                                           float* w, int32_t* counts, int32_t* assign,
+                                           int32_t* active, int32_t* rank_of,
+                                           int32_t* expert_offsets, int32_t* rank_offsets,
+                                           int32_t* pos, int32_t* src, int32_t* dedup,
+                                           void* stream) {
+  const char* fn = "moe_route_assign_layout_noalloc";
+  CHECK(check_route_assign_layout(p, logits, rep, maxrep, idx, w, counts, assign, active, rank_of,
+                                  expert_offsets, rank_offsets, pos, src, dedup, fn));
+  const size_t req = moe::route_assign_layout_ws_bytes(p->T, p->E, p->R);
+  if (req > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "%s: this problem needs %zu bytes of scratch, the static scratch holds %zu "
+                "(use moe_route_assign_layout with a workspace)", fn, req, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  CHECK(static_scratch(&ws, fn));
   clear_stale_error();
   return hip_status(moe::launch_route_assign_layout(
                         logits, p->T, p->E, p->k, p->R, rep, maxrep,

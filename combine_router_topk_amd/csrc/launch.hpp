@@ -32,6 +32,11 @@ inline size_t if_many_blocks(size_t res, long long blocks) {
 // Workspace bytes for route and layout (the larger of the two).
 size_t workspace_bytes(int T, int E, int R);
 
+// The part of that workspace launch_route_assign_layout uses: the route's
+// block rows or the layout's block matrices, without the single-send leader
+// masks.
+size_t route_assign_layout_ws_bytes(int T, int E, int R);
+
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                         int32_t* counts, int32_t* ws, hipStream_t s);
 

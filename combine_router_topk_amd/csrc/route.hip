@@ -380,6 +380,15 @@ size_t workspace_bytes(int T, int E, int R) {
   return n < 256 ? 256 : n;
 }
 
+size_t route_assign_layout_ws_bytes(int T, int E, int R) {
+  const Blocking b = blocking_for(T, E, R);
+  const size_t route = (size_t)b.route_nblk * (E + R) * sizeof(int32_t);
+  const size_t layout = (size_t)b.layout_nblk * (E + R) * sizeof(int32_t);
+  size_t n = route > layout ? route : layout;
+  n = (n + 255) & ~(size_t)255;
+  return n < 256 ? 256 : n;
+}
+
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                              int32_t* ws, hipStream_t s, int32_t* ded_rows, int R) {
   if (T == 0) return hipSuccess;

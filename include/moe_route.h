@@ -212,6 +212,36 @@ moe_status moe_route_assign_layout(const moe_problem* p, const float* logits, co
                                    int32_t* src, int32_t* dedup, void* ws, size_t ws_bytes,
                                    void* stream);
 
+/* Bytes of the static device scratch behind moe_route_assign_layout_noalloc
+ * (2 MiB per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES (2u << 20)
+
+/* moe_route_assign_layout without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The scratch is a static device
+ * array of MOE_NOALLOC_SCRATCH_BYTES that each GPU holds from the first call
+ * on it until the process ends; the call itself allocates nothing.
+ * Arguments and outputs are those of moe_route_assign_layout (the caller
+ * still allocates every input and output), and so are the results.
+ *   - A problem whose route and layout tables need more scratch than the
+ *     array holds (E + R above 1024, with enough tokens; every
+ *     problem with E + R <= 1024 fits) returns MOE_ERR_WORKSPACE before
+ *     anything is enqueued.
+ *   - The first call on a device looks up that device's copy of the array
+ *     (a failure returns MOE_ERR_HIP).
+ *   - The scratch needs no initialisation, and its contents are not
+ *     meaningful between calls.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on
+ *     one GPU (different streams, or host threads enqueueing concurrently)
+ *     race on it and give unspecified results. Order them on one stream.   */
+moe_status moe_route_assign_layout_noalloc(const moe_problem* p, const float* logits,
+                                           const int32_t* rep, int32_t maxrep, int32_t* idx,
+                                           float* w, int32_t* counts, int32_t* assign,
+                                           int32_t* active, int32_t* rank_of,
+                                           int32_t* expert_offsets, int32_t* rank_offsets,
+                                           int32_t* pos, int32_t* src, int32_t* dedup,
+                                           void* stream);
+
 /* Single-send dispatch: each token row x[t] is copied once to each distinct
  * single-send row among ss_row[t*k .. t*k+k). [CORR] section "Two locality
  * techniques".
