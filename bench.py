@@ -1,21 +1,25 @@
 """Benchmark of the single-GPU MoE routing path on MI355X.
 
 One step = one pass of the whole path over one batch resident in HBM:
-route (top-k, gate weights, demand vector) -> greedy replica assignment ->
-layout (offsets, permutation, dedup) -> dispatch -> expert stand-in ->
-combine. The headline is dispatch+combine GB/s of algorithmic bytes,
+the one-call plan (route: top-k, gate weights, demand vector; greedy
+replica assignment; layout: offsets, permutation, dedup) -> dispatch ->
+expert stand-in -> combine. The headline is dispatch+combine GB/s of algorithmic bytes,
 2 (1 + k) T H b, over the two kernels' HIP-event durations (events without
 the system-scope fence, see timing_event_type), and routed rows/s
 (T k rows over the same time). By default the 256 MB Infinity Cache and the L2s
 are flushed (a 1 GiB fill) before the dispatch and before the combine, outside
 their event brackets, so both read from HBM.
 
-After the headline loop, and outside it, the same batch also times the
-single-send variant (layout, one-row-per-rank dispatch, receiver fan-out), the
-backward of the dispatch and the combine, and the routing statistics, and
-the replicated decode workload compares the greedy replica assignment with
-token-balanced routing and times a decode step eager against a HIP graph
-replay; each is reported in its own object of the JSON line.
+After the headline loop, and outside it, every other workload is measured
+the same way (`workloads`), the same batch also times the route, assignment
+and layout as separate calls, the single-send variant (layout,
+one-row-per-rank dispatch, receiver fan-out), the backward of the dispatch
+and the combine, and the routing statistics, and the replicated decode
+workload compares the greedy replica assignment with token-balanced routing
+and times a decode step eager against a HIP graph replay; each is reported in
+its own object of the JSON line. Before any of it, and before the GPU is
+touched, the CPU oracle is timed on one core and on every usable host core
+(`cpu_baseline`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line.
@@ -59,6 +63,8 @@ def parse():
                     help="timed token-balanced splits on the replicated decode workload (0 = skip)")
     ap.add_argument("--graph-steps", type=int, default=200,
                     help="decode steps timed eager and as a HIP graph replay (0 = skip)")
+    ap.add_argument("--workload-steps", type=int, default=10,
+                    help="timed passes of every other workload, reported in `workloads` (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 30,
                     help="tokens in the oracle's CPU-baseline sample (0 = skip; default all)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -169,6 +175,85 @@ def cpu_baseline(w, seed: int, tokens: int, min_seconds: float):
             "sample": f"first {sub.T} of {w.T} tokens of {w.name}, {reps} passes; oracle dispatch + "
                       f"fp64 combine ({secs:.2f} s for {nbytes} algorithmic bytes)",
             "routed_rows_per_s": round(reps * sub.T * sub.k / secs, 1)}
+
+
+def host_cores() -> int:
+    """Host threads this process may use, at most 16 (one GPU's share of the
+    host on the GPU machines)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+_ALL = {}  # the batch the forked workers of cpu_baseline_all_cores read
+
+
+def chunk_layout(pos_all, idx, k: int, t0: int, t1: int):
+    """Send layout of tokens [t0, t1) alone: their pairs in the order they
+    have in the whole batch's send buffer, renumbered from 0 (pos), and the
+    expert of each of those rows."""
+    import numpy as np
+    pos_full = pos_all[t0 * k:t1 * k]
+    pos = np.empty_like(pos_full)
+    pos[np.argsort(pos_full, kind="stable")] = np.arange(pos_full.shape[0], dtype=pos.dtype)
+    src = np.empty_like(pos)
+    src[pos] = np.arange(pos.shape[0], dtype=pos.dtype)
+    return pos, idx[t0:t1].ravel()[src]
+
+
+def _oracle_chunk_worker(args):
+    """One worker of the all-cores leg: the oracle's dispatch and combine on
+    its own contiguous token chunk, repeated until min_seconds have passed;
+    returns (algorithmic bytes moved, seconds)."""
+    import oracle
+    t0, t1, min_seconds = args
+    d = _ALL
+    k, H = d["k"], d["H"]
+    x = d["x"][t0:t1]
+    pos, row_e = chunk_layout(d["pos"], d["idx"], k, t0, t1)
+    w = d["w"][t0:t1]
+    secs, reps = 0.0, 0
+    while reps == 0 or secs < min_seconds:
+        a = time.perf_counter()
+        send = oracle.dispatch(x, pos, k)
+        b = time.perf_counter()
+        y = oracle.expert_standin(send, row_e, d["E"], d["act"])
+        c = time.perf_counter()
+        oracle.combine(y, pos, w, k, d["act"])
+        e = time.perf_counter()
+        secs += (b - a) + (e - c)
+        reps += 1
+    return 2 * (1 + k) * (t1 - t0) * H * 2 * reps, secs
+
+
+def cpu_baseline_all_cores(w, seed: int, min_seconds: float) -> dict:
+    """The oracle, as it stands, on every usable host core at once: the batch
+    cut into one contiguous token chunk per core, each chunk's dispatch and
+    combine run by the oracle in its own process (forked before anything
+    touches the GPU), no new arithmetic. Rate = total algorithmic bytes over
+    the longest worker's timed seconds."""
+    import multiprocessing as mp
+
+    import oracle
+    import synth
+
+    logits, x = synth.make_logits(w, seed), synth.make_x(w, seed)
+    meta = oracle.route_and_layout(w.T, w.E, w.k, w.R, logits, synth.replica_table(w))
+    _ALL.update(x=x, pos=meta["pos"], idx=meta["idx"], w=meta["w"], k=w.k, H=w.H, E=w.E,
+                act=w.act_dtype)
+    n = host_cores()
+    bounds = [(w.T * i // n, w.T * (i + 1) // n, min_seconds) for i in range(n)]
+    with mp.get_context("fork").Pool(n) as pool:
+        res = pool.map(_oracle_chunk_worker, bounds)
+    _ALL.clear()
+    nbytes = sum(r[0] for r in res)
+    secs = max(r[1] for r in res)
+    return {"value": round(nbytes / secs / 1e9, 3), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": f"all {w.T} tokens of {w.name} in {n} contiguous chunks, one process per core, "
+                      f"each repeating the oracle's dispatch + fp64 combine for at least {min_seconds:.0f} s",
+            "routed_rows_per_s": round(nbytes / (2 * (1 + w.k) * w.H * 2) * w.k / secs, 1)}
 
 
 def cpu_next_rows(w, seed: int, tokens: int, min_seconds: float):
@@ -445,6 +530,65 @@ def graph_leg(P, B, synth, np, torch, dev, steps, seed):
                            "graph_us_per_step": round(fused_graph_us, 1)}}
 
 
+def workloads_leg(P, B, synth, np, torch, dev, flush, ev, seed, steps, skip) -> dict:
+    """Every other workload, measured the way the headline is: the one-call
+    plan, then dispatch and combine each after a cache flush (cold), HIP
+    events on the stream; dispatch+combine GB/s of algorithmic bytes,
+    2 (1 + k) T H b, its fraction of peak, routed rows/s, and the roofline of
+    the slower of the two kernels. The decode batch is latency-bound: its
+    stage times are the figures that matter there."""
+    out = {}
+    for w in synth.WORKLOADS:
+        if w.name == skip:
+            continue
+        logits, x = synth.make_logits(w, seed), synth.make_x(w, seed)
+        rep = synth.replica_table(w)
+        tdt = torch.float16 if w.act_dtype == synth.F16 else torch.bfloat16
+        p = B.make_problem(w.T, w.E, w.k, w.H, w.R, w.act_dtype)
+        b = P.allocate(p, torch.from_numpy(logits), torch.from_numpy(x.view(np.int16)).view(tdt),
+                       None if rep is None else torch.from_numpy(rep), device=dev)
+        del logits, x
+        marks = []
+        for i in range(steps + 2):
+            e = [ev() for _ in range(6)]
+            if flush is not None:
+                flush.fill_(9.0)
+            e[0].record()
+            P.route_assign_layout(b)
+            e[1].record()
+            if flush is not None:
+                flush.fill_(10.0)
+            e[2].record()
+            P.dispatch(b)
+            e[3].record()
+            P.standin(b)
+            if flush is not None:
+                flush.fill_(11.0)
+            e[4].record()
+            P.combine(b)
+            e[5].record()
+            if i >= 2:
+                marks.append(e)
+        torch.cuda.synchronize()
+        avg = lambda i: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks]))
+        plan_ms, d_ms, c_ms = avg(0), avg(2), avg(4)
+        half = (1 + w.k) * w.T * w.H * 2
+        dc = 2 * half
+        dom, dom_ms = ("dispatch_kernel", d_ms) if d_ms >= c_ms else ("combine_kernel", c_ms)
+        gbps = dc / ((d_ms + c_ms) / 1e3) / 1e9
+        out[w.name] = {
+            "stage_us": {"plan": round(plan_ms * 1e3, 2), "dispatch": round(d_ms * 1e3, 2),
+                         "combine": round(c_ms * 1e3, 2)},
+            "dispatch_combine_GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4),
+            "routed_rows_per_s": round(w.T * w.k / ((d_ms + c_ms) / 1e3), 1),
+            "roofline": {"bound": "hbm", "kernel": dom,
+                         "achieved": round(half / (dom_ms / 1e3) / 1e9, 1), "peak": PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(half / (dom_ms / 1e3) / 1e9 / PEAK_GBPS, 4)}}
+        del b
+        torch.cuda.empty_cache()
+    return out
+
+
 def separate_calls_leg(P, b, flush, steps, ev, np, torch) -> dict:
     """Route, assignment and layout as three separate calls (the kernels of
     moe_route, moe_assign_replicas and moe_layout), each bracketed by events,
@@ -502,6 +646,13 @@ def main():
     from combine_router_topk_amd import path as P
 
     w = synth.BY_NAME[args.workload]
+    # the oracle legs run first: the all-cores leg forks worker processes,
+    # which must happen before this process touches the GPU
+    cpu = None
+    if args.cpu_tokens > 0:
+        cpu = cpu_baseline(w, args.seed, args.cpu_tokens, args.cpu_seconds)
+        cpu["all_cores"] = cpu_baseline_all_cores(w, args.seed, args.cpu_seconds)
+        cpu["next_rows"] = cpu_next_rows(w, args.seed, args.cpu_tokens, args.cpu_seconds / 4)
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     logits = synth.make_logits(w, args.seed)
@@ -627,6 +778,9 @@ def main():
                      "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": traffic},
     }
+    if args.workload_steps > 0:
+        res["workloads"] = workloads_leg(P, B, synth, np, torch, dev, flush, ev, args.seed,
+                                         args.workload_steps, w.name)
     if flush is not None and args.warm_steps > 0:
         res["warm_cache"] = warm_leg(P, b, args.warm_steps, ev, np, torch, dc_bytes)
     if args.single_send_steps > 0:
@@ -640,10 +794,8 @@ def main():
         res["eplb"] = eplb_leg(P, B, synth, np, torch, dev, args.eplb_steps, ev, args.seed)
     if args.graph_steps > 0:
         res["decode_graph"] = graph_leg(P, B, synth, np, torch, dev, args.graph_steps, args.seed)
-    if args.cpu_tokens > 0:
-        res["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_tokens, args.cpu_seconds)
-        res["cpu_baseline"]["next_rows"] = cpu_next_rows(w, args.seed, args.cpu_tokens,
-                                                         args.cpu_seconds / 4)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

@@ -55,3 +55,28 @@ def test_path_summary_arithmetic():
     assert abs(s["GBps"] - want / 100e-6 / 1e9) < 0.01
     assert s["metadata_share_of_time"] == 0.2
     assert abs(s["routed_rows_per_s"] - 32768 / 100e-6) < 1
+
+
+def test_cpu_all_cores_fields():
+    w = synth.scaled(synth.TRAIN_TOP2, T=96, H=64)
+    c = bench.cpu_baseline_all_cores(w, 0, 0.0)
+    assert c["unit"] == "GB/s" and c["kind"] == "oracle" and c["value"] > 0
+    assert 1 <= c["cores"] <= 16 and c["cores"] == bench.host_cores()
+    assert c["routed_rows_per_s"] > 0
+
+
+def test_oracle_chunk_worker_keeps_the_full_layout_order():
+    """A worker's chunk is dispatched in the order its pairs have in the
+    whole send buffer: its rows are the whole batch's rows of those tokens."""
+    import numpy as np
+    import oracle
+    w = synth.scaled(synth.TRAIN_TOP6, T=40, H=16)
+    logits, x = synth.make_logits(w, 0), synth.make_x(w, 0)
+    m = oracle.route_and_layout(w.T, w.E, w.k, w.R, logits)
+    full = oracle.dispatch(x, m["pos"], w.k)
+    t0, t1 = 7, 23
+    loc, row_e = bench.chunk_layout(m["pos"], m["idx"], w.k, t0, t1)
+    part = oracle.dispatch(x[t0:t1], loc, w.k)
+    rows = np.sort(m["pos"][t0 * w.k:t1 * w.k])
+    assert np.array_equal(part, full[rows])
+    assert np.array_equal(row_e, m["idx"].ravel()[m["src"][rows]])
