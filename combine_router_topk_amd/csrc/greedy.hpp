@@ -35,9 +35,16 @@ constexpr int kMaxRep = 16;  // replica-table columns (the C ABI caps maxrep)
 // themselves live in a register (lane g holds act[g] << 16 | g, at most 64
 // GPUs), so a candidate's key is one readlane; else the counters are in LDS.
 // Every value that decides a choice is wave-uniform.
+// `gpus` (IN_REG only) restricts the walk to the experts whose candidates lie
+// in that set of GPUs (tested on the first candidate), and only those GPUs'
+// counters are written back: walkers given disjoint unions of whole
+// components of the GPU graph (GPUs joined by a shared expert) make the
+// same choices as one walker, since an expert's choice reads and changes
+// only counters of its own component.
 template <bool IN_REG>
-__device__ void greedy_walk(int E, int maxrep, int id_order, const unsigned char* ncand,
-                            const unsigned short* cand, int* act, int32_t* __restrict__ assign) {
+__device__ __forceinline__ void greedy_walk(int E, int maxrep, int id_order, const unsigned char* ncand,
+                                            const unsigned short* cand, int* act,
+                                            int32_t* __restrict__ assign, uint64_t gpus = ~0ull) {
   const int lane = threadIdx.x & (kWave - 1);
   // lanes >= R hold keys never read
   uint32_t key_reg = IN_REG ? (static_cast<uint32_t>(act[lane]) << 16) | static_cast<uint32_t>(lane) : 0u;
@@ -47,7 +54,8 @@ __device__ void greedy_walk(int E, int maxrep, int id_order, const unsigned char
     for (int base = 0; base < E; base += kWave) {
       const int e = base + lane;
       const int ce = e < E ? ncand[e] : 0;
-      uint64_t m = ballot(c == 0 ? ce > 0 : ce == c);
+      const int g_first = ce > 0 ? cand[e * kMaxRep] : 0;
+      uint64_t m = ballot((c == 0 ? ce > 0 : ce == c) && ((gpus >> (g_first & 63)) & 1ull));
       if (m == 0ull) continue;
       uint32_t cpk[kMaxRep / 2];  // this lane's expert: candidates as 16-bit pairs
 #pragma unroll
@@ -77,7 +85,34 @@ __device__ void greedy_walk(int E, int maxrep, int id_order, const unsigned char
       }
     }
   }
-  if (IN_REG) act[lane] = static_cast<int>(key_reg >> 16);  // act holds at least 64 entries (see assign_block)
+  // act holds at least 64 entries (see assign_block)
+  if (IN_REG && ((gpus >> lane) & 1ull)) act[lane] = static_cast<int>(key_reg >> 16);
+}
+
+// The components of the GPU graph in which two GPUs are joined when some
+// walked expert has both as candidates, found by one wave (R <= 64, lane g
+// for GPU g): adj is each GPU's union of the candidate sets of the walked
+// experts that list it (symmetric, so a GPU joins a component exactly when
+// its adj meets it, one ballot per step). Component i, in the order of their
+// lowest GPU, goes to walker i % walkers; returns the GPUs of `walker`'s
+// components. Wave-uniform.
+__device__ __forceinline__ uint64_t walker_gpus(const unsigned long long* adj, int R, int walker,
+                                                int walkers) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t a = lane < R ? adj[lane] : 0ull;
+  uint64_t todo = ballot(a != 0ull);
+  uint64_t mine = 0ull;
+  for (int i = 0; todo != 0ull; ++i) {
+    uint64_t comp = 1ull << __builtin_ctzll(todo);
+    for (;;) {
+      const uint64_t grown = comp | ballot((a & comp) != 0ull);
+      if (grown == comp) break;
+      comp = grown;
+    }
+    if (i % walkers == walker) mine |= comp;
+    todo &= ~comp;
+  }
+  return mine;
 }
 
 // The whole assignment by one 1024-thread workgroup. counts [E] (read) and

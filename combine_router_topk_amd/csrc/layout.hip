@@ -710,6 +710,287 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_permute_scan_kernel(
   permute_rounds<WAVES>(idx, i0, i1, E, T * k, run, wcnt, wtag, pos, src);
 }
 
+// The routing plan of a decode-sized batch (T <= 1024 tokens, T k <= 8192
+// pairs) after the top-k kernel, in one workgroup with one round trip to
+// global memory: the route's histogram rows, the expert ids and the replica
+// rows are all loaded at the start. A pair's place inside its expert's
+// segment does not depend on the assignment, so it is computed while the
+// greedy walks: each expert gets a bitmask of the tokens that chose it, and
+// the place of pair (t, e) is the number of bits of e's mask below t (a token
+// chooses an expert at most once, so this is the stable rank). Wave 0 walks
+// the multi-copy experts in order (greedy_walk) while waves 1..15 count
+// those bits. Then the ranks of the experts, the per-token dedup counts and
+// the offsets (finish_few_ranks for up to 64 ranks, else plan_finish), and
+// pos = expert offset + place.
+// Outputs equal those of route_plan_small_kernel.
+constexpr int kMaskMaxT = 1024;
+constexpr int kMaskPairsPerThread = kSmallPairs / kPlanThreads;
+
+__host__ __device__ constexpr int round4(int n) { return (n + 3) & ~3; }
+
+__host__ __device__ constexpr int mask_plan_ints(int T, int E, int k, int R) {
+  const int W = (T + 63) / 64, e8 = (E + 8) & ~7;
+  return round4(2 * W * E) + 2 * round4(e8) + 2 * round4(E) + 3 * round4(R) +
+         round4(R > kWave ? R : kWave) + round4((E + 3) / 4) + round4(E * kMaxRep / 2) +
+         2 * round4((T * k + 1) / 2) +
+         (R <= kWave ? round4(kPlanWaves * R) + round4(R + 1) + 2 * round4(E) + 2 * kWave : 0);
+}
+
+// The end of the bitmask plan for at most 64 ranks, after s_rank holds every
+// expert's rank (all threads take part; ends with a barrier):
+//  - dedup: each token's ranks as a 64-bit set, counted per rank with one
+//    ballot per rank and wave;
+//  - the experts in (rank, id) order: each expert's place among the experts
+//    of its rank from ballot matching on the rank bits (lower lanes) and
+//    per-wave counts (earlier waves), plus the experts of lower ranks;
+//  - one block scan of the counts in that order gives every expert's offset,
+//    and a rank's offset is the scan at its first place.
+// s_wr [16][R], s_rbase [R + 1], s_ord [E], s_scan [E] are LDS scratch
+// (s_wr zeroed by the caller).
+__device__ __forceinline__ void finish_few_ranks(
+    int T, int E, int k, int R, const int* s_rank, const int* s_counts,
+    const unsigned short* s_idx, int* s_ded, int* s_wr, int* s_rbase, int* s_ord, int* s_scan,
+    int* s_eoff, int* s_wave, int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ dedup) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  if (wave < (T + kWave - 1) / kWave) {  // uniform per wave
+    // the token's ids are read with loads issued together (slots past k
+    // reread slot k - 1), then their ranks
+    unsigned long long rm = 0ull;
+    if (tid < T) {
+      int ids[kMaxK];
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) ids[j] = s_idx[tid * k + (j < k ? j : k - 1)];
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) rm |= 1ull << s_rank[ids[j]];
+    }
+    for (int r = 0; r < R; ++r) {
+      const int c = __popcll(ballot((rm >> r) & 1ull));
+      if (lane == 0 && c > 0) atomicAdd(&s_ded[r], c);
+    }
+  }
+  const int r = tid < E ? s_rank[tid] : R;  // R: past every rank
+  const int nbits = 32 - __builtin_clz(static_cast<unsigned>(R));
+  uint64_t peers = ballot(true);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool x = (r >> bit) & 1;
+    const uint64_t m = ballot(x);
+    peers &= x ? m : ~m;
+  }
+  const int within = __popcll(peers & lanemask_lt(lane));
+  if (tid < E && __builtin_ctzll(peers) == lane) s_wr[wave * R + r] = __popcll(peers);
+  __syncthreads();
+  if (wave == 0) {
+    int ne = 0;
+    if (lane < R)
+      for (int w = 0; w < kPlanWaves; ++w) ne += s_wr[w * R + lane];
+    const int incl = wave_incl_scan(ne, lane);
+    if (lane < R) {
+      s_rbase[lane] = incl - ne;
+      dedup[lane] = s_ded[lane];
+    }
+  }
+  __syncthreads();
+  int place = 0;
+  if (tid < E) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += s_wr[w * R + r];
+    place = s_rbase[r] + before + within;
+    s_ord[place] = s_counts[tid];
+    rank_of[tid] = r;
+  }
+  __syncthreads();
+  int total = 0;
+  const int ex = block_excl_scan(tid < E ? s_ord[tid] : 0, s_wave, &total);
+  if (tid < E) s_scan[tid] = ex;
+  __syncthreads();
+  if (tid < E) {
+    const int o = s_scan[place];
+    expert_offsets[tid] = o;
+    s_eoff[tid] = o;
+  }
+  if (tid < R) rank_offsets[tid] = s_rbase[tid] < E ? s_scan[s_rbase[tid]] : total;
+  if (tid == 0) rank_offsets[R] = total;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
+    const int32_t* __restrict__ hist, int nblk, const int32_t* __restrict__ idx, int T, int E,
+    int k, int R, const int32_t* __restrict__ rep, int maxrep, int id_order,
+    int32_t* __restrict__ counts, int32_t* __restrict__ assign, int32_t* __restrict__ active,
+    int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pos, int32_t* __restrict__ src,
+    int32_t* __restrict__ dedup) {
+  extern __shared__ __align__(16) int smem[];
+  __shared__ int s_wave[kPlanWaves];
+  __shared__ int s_wave2[kPlanWaves];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int W = (T + 63) / 64;  // mask words per expert
+  const int n = T * k;
+  const int e8 = (E + 8) & ~7;
+  unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);  // [E][W]
+  int* p = smem + round4(2 * W * E);
+  int* s_counts = p; p += round4(e8);  // the demand vector (plan_finish pads it)
+  int* s_rank = p;   p += round4(e8);
+  int* s_eoff = p;   p += round4(E);
+  int* s_assign = p; p += round4(E);
+  int* s_ded = p;    p += round4(R);
+  int* s_rtok = p;   p += round4(R);
+  int* s_roff = p;   p += round4(R);
+  int* act = p;      p += round4(R > kWave ? R : kWave);
+  unsigned char* ncand = reinterpret_cast<unsigned char*>(p); p += round4((E + 3) / 4);
+  unsigned short* cand = reinterpret_cast<unsigned short*>(p); p += round4(E * kMaxRep / 2);
+  unsigned short* s_idx = reinterpret_cast<unsigned short*>(p); p += round4((n + 1) / 2);
+  unsigned short* s_rk = reinterpret_cast<unsigned short*>(p); p += round4((n + 1) / 2);
+  const bool few = R <= kWave;  // the ballot-based end (finish_few_ranks)
+  int* s_wr = p;    p += few ? round4(kPlanWaves * R) : 0;
+  int* s_rbase = p; p += few ? round4(R + 1) : 0;
+  int* s_ord = p;   p += few ? round4(E) : 0;
+  int* s_scan = p;  p += few ? round4(E) : 0;
+  unsigned long long* adj = reinterpret_cast<unsigned long long*>(p);  // [64] when few
+
+  // every global load first: histogram column partials (eight rows per
+  // thread issued together, a loop for any further rows), expert ids,
+  // replica rows
+  const int groups = E >= kPlanThreads ? 1 : kPlanThreads / E;
+  const int col = tid % E, grp = tid / E;
+  int part = 0;
+  if (grp < groups) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = grp + i * groups;
+      v[i] = r < nblk ? hist[(size_t)r * E + col] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part += v[i];
+    for (int r = grp + 8 * groups; r < nblk; r += groups) part += hist[(size_t)r * E + col];
+  }
+  int pe[kMaskPairsPerThread];
+#pragma unroll
+  for (int j = 0; j < kMaskPairsPerThread; ++j) {
+    const int i = tid + j * kPlanThreads;
+    pe[j] = i < n ? clamp_expert(idx[i], E) : 0;
+  }
+  int rr[kMaxRep];
+#pragma unroll
+  for (int s = 0; s < kMaxRep; ++s)
+    rr[s] = (rep != nullptr && tid < E && s < maxrep) ? rep[tid * maxrep + s] : -1;
+
+  for (int i = tid; i < W * E; i += kPlanThreads) mask[i] = 0ull;
+  for (int i = tid; i < e8; i += kPlanThreads) s_counts[i] = 0;
+  for (int i = tid; i < R; i += kPlanThreads) {
+    s_ded[i] = 0;
+    s_rtok[i] = 0;
+  }
+  for (int i = tid; i < (R > kWave ? R : kWave); i += kPlanThreads) act[i] = 0;
+  if (few) {
+    for (int i = tid; i < kPlanWaves * R; i += kPlanThreads) s_wr[i] = 0;
+    if (tid < kWave) adj[tid] = 0ull;
+  }
+  __syncthreads();
+  if (grp < groups && part != 0) atomicAdd(&s_counts[col], part);
+#pragma unroll
+  for (int j = 0; j < kMaskPairsPerThread; ++j) {
+    const int i = tid + j * kPlanThreads;
+    if (i < n) {
+      const int t = i / k;
+      atomicOr(&mask[pe[j] * W + (t >> 6)], 1ull << (t & 63));
+      s_idx[i] = static_cast<unsigned short>(pe[j]);
+    }
+  }
+  __syncthreads();
+  // active experts: their valid candidates to LDS; single-copy experts (and
+  // every expert without a table) are placed at once
+  if (tid < E) {
+    const int c = s_counts[tid];
+    counts[tid] = c;
+    if (rep == nullptr) {
+      const int per = E / R;
+      s_assign[tid] = c > 0 ? tid / per : -1;
+      if (c > 0) atomicAdd(&act[tid / per], 1);
+    } else {
+      int nc = 0;
+      if (c > 0) {
+#pragma unroll
+        for (int s = 0; s < kMaxRep; ++s)
+          if (rr[s] >= 0 && rr[s] < R) cand[tid * kMaxRep + nc++] = static_cast<unsigned short>(rr[s]);
+      }
+      ncand[tid] = static_cast<unsigned char>(nc);
+      if (nc == 0) s_assign[tid] = -1;
+      if (!id_order && nc == 1) {
+        s_assign[tid] = cand[tid * kMaxRep];
+        atomicAdd(&act[cand[tid * kMaxRep]], 1);
+      }
+      // the GPU graph of the walked experts: each candidate learns the others
+      if (few && nc >= (id_order ? 1 : 2)) {
+        unsigned long long cm = 0ull;
+        for (int q = 0; q < nc; ++q) cm |= 1ull << cand[tid * kMaxRep + q];
+        for (int q = 0; q < nc; ++q) atomicOr(&adj[cand[tid * kMaxRep + q]], cm);
+      }
+    }
+  }
+  __syncthreads();
+  // With at most 64 GPUs the walk is split over waves 0..3 (one per SIMD),
+  // each taking whole components of the GPU graph, and waves 4..15 find the
+  // pairs' places; else wave 0 walks and waves 1..15 find the places.
+  const int walkers = (few && rep != nullptr) ? 4 : 1;
+  if (wave < walkers) {
+    if (rep != nullptr) {
+      if (few) {
+        const uint64_t gpus = walker_gpus(adj, R, wave, walkers);
+        if (gpus != 0ull) greedy_walk<true>(E, maxrep, id_order, ncand, cand, act, s_assign, gpus);
+      } else {
+        greedy_walk<false>(E, maxrep, id_order, ncand, cand, act, s_assign);
+      }
+    }
+  } else {
+    // place of each pair inside its expert: earlier tokens in the expert's mask
+    for (int i = tid - walkers * kWave; i < n; i += kPlanThreads - walkers * kWave) {
+      const int e = s_idx[i], t = i / k, wt = t >> 6;
+      const unsigned long long* m = mask + e * W;
+      int c = __popcll(m[wt] & ((1ull << (t & 63)) - 1ull));
+      for (int q = 0; q < wt; ++q) c += __popcll(m[q]);
+      s_rk[i] = static_cast<unsigned short>(c);
+    }
+  }
+  __syncthreads();
+  if (tid < E) {
+    assign[tid] = s_assign[tid];
+    s_rank[tid] = expert_rank(tid, E, R, s_assign, rep, maxrep);
+  }
+  for (int g = tid; g < R; g += kPlanThreads) active[g] = act[g];
+  __syncthreads();
+  if (few) {
+    finish_few_ranks(T, E, k, R, s_rank, s_counts, s_idx, s_ded, s_wr, s_rbase, s_ord, s_scan,
+                     s_eoff, s_wave, rank_of, expert_offsets, rank_offsets, dedup);
+  } else {
+    if (tid < T) {  // distinct destination ranks of the token
+      int rk[kMaxK];
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) rk[j] = j < k ? s_rank[s_idx[tid * k + j]] : -1 - j;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        bool seen = false;
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj) seen |= (rk[jj] == rk[j]);
+        if (j < k && !seen) atomicAdd(&s_ded[rk[j]], 1);
+      }
+    }
+    plan_finish(E, R, s_rank, s_counts, s_ded, s_rtok, s_roff, s_wave, s_wave2, rank_of,
+                expert_offsets, rank_offsets, dedup, nullptr, s_eoff, nullptr);
+    __syncthreads();
+  }
+  for (int i = tid; i < n; i += kPlanThreads) {
+    const int q = s_eoff[s_idx[i]] + s_rk[i];
+    pos[i] = q;
+    if (static_cast<unsigned>(q) < static_cast<unsigned>(n)) src[q] = i;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_layout(const int32_t* idx, int T, int E, int k, int R, const int32_t* assign,
@@ -779,6 +1060,16 @@ hipError_t launch_route_assign_layout(const float* logits, int T, int E, int k, 
                                       int32_t* rank_offsets, int32_t* pos, int32_t* src,
                                       int32_t* dedup, int32_t* ws, hipStream_t s) {
   const size_t plan_ints = plan_small_ints(E, R);
+  if (T > 0 && T <= kMaskMaxT && (int64_t)T * k <= kSmallPairs &&
+      mask_plan_ints(T, E, k, R) <= kSmallLdsInts) {
+    hipError_t err = launch_route_topk(logits, T, E, k, idx, w, ws, s);
+    if (err != hipSuccess) return err;
+    route_plan_mask_kernel<<<1, kPlanThreads, mask_plan_ints(T, E, k, R) * sizeof(int), s>>>(
+        ws, blocking_for(T, E, R).route_nblk, idx, T, E, k, R, rep, rep ? maxrep : 1,
+        id_order ? 1 : 0, counts, assign, active, rank_of, expert_offsets, rank_offsets, pos, src,
+        dedup);
+    return hipGetLastError();
+  }
   if (T > 0 && (int64_t)T * k <= kSmallPairs && plan_ints <= kSmallLdsInts) {
     hipError_t err = launch_route_topk(logits, T, E, k, idx, w, ws, s);
     if (err != hipSuccess) return err;

@@ -113,6 +113,9 @@ EDGE = [
     ("E1024_R1024_LDS_too_small", 200, 1024, 16, 1024),   # the three calls' kernels
     ("T2000_k8_past_8192_pairs", 2000, 256, 8, 32),      # the three calls' kernels
     ("T8192_k1_at_8192_pairs", 8192, 16, 1, 4),          # the largest two-launch batch
+    ("T1024_k8_mask_plan_limit", 1024, 64, 8, 8),        # the largest bitmask plan
+    ("T1025_k7_small_plan", 1025, 64, 7, 8),             # one token past it
+    ("T300_E256_R128", 300, 256, 4, 128),                # bitmask plan, 128 ranks
 ]
 
 
