@@ -162,3 +162,41 @@ def test_graph_of_the_fused_pass_replays_bit_for_bit():
                 tb, te = tb.view(torch.int16 if tb.element_size() == 2 else torch.int32), \
                     te.view(torch.int16 if te.element_size() == 2 else torch.int32)
             assert torch.equal(tb, te), (seed, name)
+
+
+def component_table(E, R, groups, maxrep, rng):
+    """A replica table whose experts only list GPUs of one group, so the GPU
+    graph splits into `groups` components (more or fewer than the decode
+    plan's four walkers); every expert's copies are in a random order."""
+    per = R // groups
+    rep = np.full((E, maxrep), -1, np.int32)
+    for e in range(E):
+        g = e % groups
+        n = int(rng.integers(1, min(maxrep, per) + 1))
+        rep[e, :n] = g * per + rng.choice(per, size=n, replace=False)
+    return rep
+
+
+@pytest.mark.parametrize("order", ["constrained", "id"])
+@pytest.mark.parametrize("groups", [1, 3, 6, 16])
+def test_decode_plan_walkers_over_gpu_components(groups, order):
+    """The decode plan splits the greedy walk over four waves by components of
+    the GPU graph: one component (one walker), three (one walker idle), six
+    and sixteen (walkers taking several) must all give the single-walker
+    result, which the oracle's sequential greedy defines."""
+    rng = np.random.default_rng(40 + groups)
+    E, R = 96, 48
+    rep = component_table(E, R, groups, 3, rng)
+    w = synth.Workload(f"components{groups}", 400, E, 6, 8, R, synth.BF16, "zipf1.2", False)
+    run_both(w, 7, rep=rep, order=order)
+
+
+@pytest.mark.parametrize("order", ["constrained", "id"])
+def test_decode_plan_without_two_copy_experts(order):
+    """A table where every expert has one copy: nothing to walk in the default
+    order (every walker gets no GPUs), every expert walked in the id order."""
+    E, R = 64, 16
+    rep = np.full((E, 2), -1, np.int32)
+    rep[:, 0] = (np.arange(E) * 7) % R
+    w = synth.Workload("one_copy_each", 256, E, 4, 8, R, synth.F16, "none", False)
+    run_both(w, 8, rep=rep, order=order)
