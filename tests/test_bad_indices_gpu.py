@@ -159,3 +159,44 @@ def test_out_of_range_expert_ids_are_clamped(T, E, k, R):
     assert np.array_equal(host(b.expert_offsets), eo) and np.array_equal(host(b.rank_offsets), ro)
     assert np.array_equal(host(b.pos), pos) and np.array_equal(host(b.src), src)
     assert np.array_equal(host(b.dedup), oracle.dedup_counts(clamped, rank_of, R))
+
+
+@pytest.mark.parametrize("T,E,k,R", [(256, 256, 8, 8), (1500, 64, 5, 8), (12000, 64, 4, 16)],
+                         ids=["bitmask_plan", "small_plan", "three_calls"])
+def test_out_of_range_replica_entries_stay_in_bounds(T, E, k, R):
+    """Replica entries outside [-1, R) (about 10% of them, the primary copy
+    included) give an unspecified assignment, but the one-call plan keeps
+    every access in bounds and its outputs well formed: assign in [-1, R)
+    and only on an active expert, rank_of in [0, R), active summing to the
+    experts placed, offsets consistent with the counts, pos a permutation
+    of the send rows with src its inverse."""
+    rng = np.random.default_rng(T + E)
+    maxrep = 3
+    rep = np.full((E, maxrep), -1, np.int64)
+    for e in range(E):
+        n = int(rng.integers(1, maxrep + 1))
+        rep[e, :n] = rng.choice(R, size=n, replace=False)
+    bad = rng.random(rep.shape) < 0.1
+    vals = np.array([R, R + 5, -7, 2**31 - 1, -2**31], np.int64)
+    rep[bad] = vals[rng.integers(len(vals), size=int(bad.sum()))]
+    rep = rep.astype(np.int32)
+    w = synth.Workload("bad_rep", T, E, k, 8, R, synth.BF16, "zipf1.2", False)
+    say(f"[case] out-of-range replica entries T={T} E={E} k={k} R={R}")
+    p = B.make_problem(T, E, k, 8, R, w.act_dtype)
+    b = P.allocate(p, torch.from_numpy(synth.make_logits(w, 3)), torch.zeros(T, 8, dtype=torch.bfloat16),
+                   torch.from_numpy(rep))
+    P.route_assign_layout(b)
+    torch.cuda.synchronize()
+    counts, assign = host(b.counts), host(b.assign)
+    assert counts.sum() == T * k
+    assert ((assign >= -1) & (assign < R)).all()
+    assert ((assign >= 0) <= (counts > 0)).all()          # only active experts are placed
+    assert host(b.active).sum() == int((assign >= 0).sum())
+    rank_of = host(b.rank_of)
+    assert ((rank_of >= 0) & (rank_of < R)).all()
+    n = T * k
+    pos, src = host(b.pos).astype(np.int64), host(b.src).astype(np.int64)
+    assert np.array_equal(np.sort(pos), np.arange(n)) and np.array_equal(src[pos], np.arange(n))
+    ro = host(b.rank_offsets)
+    assert ro[0] == 0 and ro[-1] == n
+    assert np.array_equal(np.diff(ro), np.bincount(rank_of, counts, minlength=R).astype(np.int64))
