@@ -31,6 +31,17 @@
 //   in one launch, when the single-send rows are asked for.)
 // A small batch (T k <= 8192 pairs) runs all of it in one workgroup instead
 // (layout_small), sharing the same device functions.
+//
+// The one-call route + assignment + layout (launch_route_assign_layout)
+// picks, after the top-k kernel:
+//  - a decode-sized batch (T <= 1024, T k <= 8192): route_plan_mask_kernel,
+//    one workgroup with one round trip to global memory, the pairs' places
+//    from per-expert token bitmasks counted while the greedy walks;
+//  - a batch of up to 8192 pairs whose tables fit: route_plan_small_kernel;
+//  - a larger batch without a replica table: plan_scan_kernel and
+//    layout_permute_scan_kernel, from the top-k kernel's per-block expert
+//    and rank rows (three launches in all);
+//  - else the kernels of the separate route, assignment and layout calls.
 #include "device.hpp"
 #include "greedy.hpp"
 #include "launch.hpp"
