@@ -200,11 +200,15 @@ moe_status moe_layout_single_send(const moe_problem* p, const int32_t* idx, cons
  * both an output and the layout's input). For a decode batch fixed latency
  * rather than bytes sets the time ([METRO] section "Find the crossover
  * instead of copying 2 MB": below the crossover payload a fixed overhead
- * dominates), so the steps share launches. A batch with T*k <= 8192 whose tables fit in 64 KiB
- * of LDS takes two launches: the top-k kernel, then one workgroup that sums
- * the demand vector, runs the greedy and lays out the batch. Larger batches
- * take the kernels of the three separate calls. ws is one workspace of
- * moe_workspace_bytes().                                                   */
+ * dominates), so the steps share launches:
+ *   - a batch with T*k <= 8192 whose tables fit in 64 KiB of LDS: two
+ *     launches, the top-k kernel, then one workgroup that sums the demand
+ *     vector, runs the greedy and lays out the batch;
+ *   - a larger batch without a replica table (rep NULL): three launches,
+ *     the top-k kernel (which also counts each block's tokens per rank), a
+ *     column scan, and the permutation;
+ *   - a larger batch with a replica table: the kernels of the three calls.
+ * ws is one workspace of moe_workspace_bytes().                             */
 moe_status moe_route_assign_layout(const moe_problem* p, const float* logits, const int32_t* rep,
                                    int32_t maxrep, int32_t* idx, float* w, int32_t* counts,
                                    int32_t* assign, int32_t* active, int32_t* rank_of,
