@@ -123,3 +123,21 @@ def test_empty_batch():
     assert m["counts"].tolist() == [0] * 8 and m["active"].tolist() == [0] * 4
     assert m["rank_offsets"].tolist() == [0] * 5 and m["dedup"].tolist() == [0] * 4
     assert (m["assign"] == -1).all()
+
+
+def test_inactive_experts_sit_on_their_first_listed_copy():
+    """Worked by hand: an expert without rows keeps its primary copy (the
+    first entry of its replica row, here a higher GPU than its second copy),
+    not its lowest or last-listed one; with no rows it moves no offset.
+    E = 4 on 3 GPUs, rows [[2, 0], [1, -], [0, 2], [1, 2]], counts [0, 5, 0, 3]:
+    expert 1 (one copy) goes to GPU 1, expert 3 to GPU 2 (0 activated against
+    1); experts 0 and 2 are inactive and sit on GPUs 2 and 0. Send order
+    (rank, id): expert 2 (0 rows), expert 1 (5), expert 0 (0), expert 3 (3)."""
+    rep = np.array([[2, 0], [1, -1], [0, 2], [1, 2]], np.int32)
+    counts = np.array([0, 5, 0, 3], np.int32)
+    assign, act = oracle.greedy_assign(counts, 3, rep)
+    assert assign.tolist() == [-1, 1, -1, 2] and act.tolist() == [0, 1, 1]
+    rank_of = oracle.expert_ranks(4, 3, rep, assign)
+    assert rank_of.tolist() == [2, 1, 0, 2]
+    eo, ro = oracle.segment_offsets(counts, rank_of, 3)
+    assert eo.tolist() == [5, 0, 0, 5] and ro.tolist() == [0, 0, 5, 8]

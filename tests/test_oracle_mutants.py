@@ -22,7 +22,7 @@ import test_oracle_stats as TT
 from oracle.rows import BF16
 
 O = {name: getattr(oracle, name) for name in (
-    "topk_select", "gate_weights", "demand_vector", "greedy_assign", "permutation",
+    "topk_select", "gate_weights", "demand_vector", "greedy_assign", "permutation", "expert_ranks",
     "segment_offsets", "dedup_counts", "encode16", "expert_standin", "combine",
     "single_send_layout", "gini", "coselection", "routing_stats")}
 O["replica_share_index"] = oracle.eplb.replica_share_index
@@ -95,6 +95,16 @@ def greedy_ties_to_first_listed_replica(counts, R, rep, order="constrained"):
         assign[e] = cand[e][slot]
         active[assign[e]] += 1
     return np.array(assign, dtype=np.int32), np.array(active, dtype=np.int32)
+
+
+def inactive_experts_on_last_copy(E, R, rep, assign):
+    cand = oracle.candidates(E, R, rep)
+    primary = np.array([c[0] for c in cand], dtype=np.int32)
+    if assign is None:
+        return primary
+    last = np.array([c[-1] for c in cand], dtype=np.int32)
+    assign = np.asarray(assign)
+    return np.where(assign >= 0, assign, last).astype(np.int32)
 
 
 def greedy_always_id_order(counts, R, rep, order="constrained"):
@@ -191,6 +201,8 @@ CASES = [
       (TP.test_greedy_does_not_depend_on_replica_slot_order, (0,))]),
     ("greedy ignores the most-constrained order", "greedy_assign", greedy_always_id_order,
      [(TP.test_decode_table_all_active_closed_form, ("constrained", "active_constrained_order"))]),
+    ("inactive experts on their last-listed copy", "expert_ranks", inactive_experts_on_last_copy,
+     [(TL.test_inactive_experts_sit_on_their_first_listed_copy, ())]),
     ("tokens descending inside an expert", "permutation", permutation_tokens_descending,
      [(TL.test_handworked_layouts, ()), (TL.test_layout_bruteforce_random, (3,))]),
     ("inclusive expert offsets", "segment_offsets", offsets_inclusive,
