@@ -499,7 +499,10 @@ def graph_leg(P, B, synth, np, torch, dev, steps, seed):
     small and the host's launches set the pace: wall time per step for eager
     calls against one replay of a HIP graph holding the same pass (warm
     cache, the stream drained after each step in both cases), also with
-    route, assign and layout as one call (`fused_plan`)."""
+    route, assign and layout as one call (`fused_plan`). `pipelined_us_per_step`
+    issues the steps back to back and drains the stream once at the end, as
+    a loop over layers does: the device's own time per step once the host's
+    launch and synchronisation are off the critical path."""
     w = synth.DECODE
     logits, x = synth.make_logits(w, seed), synth.make_x(w, seed)
     rep = synth.replica_table(w)
@@ -520,14 +523,28 @@ def graph_leg(P, B, synth, np, torch, dev, steps, seed):
             torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps * 1e6
 
+    def pipelined(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e6
+
     eager_us = timed(lambda: P.run(b))
     graph_us = timed(g.replay)
     fused_eager_us = timed(lambda: [step(b) for step in P.FUSED_STEPS])
     fused_graph_us = timed(gf.replay)
+    graph_pipe_us = pipelined(g.replay)
+    fused_graph_pipe_us = pipelined(gf.replay)
     return {"workload": w.name, "steps": steps, "eager_us_per_step": round(eager_us, 1),
             "graph_us_per_step": round(graph_us, 1),
+            "graph_pipelined_us_per_step": round(graph_pipe_us, 1),
             "fused_plan": {"eager_us_per_step": round(fused_eager_us, 1),
-                           "graph_us_per_step": round(fused_graph_us, 1)}}
+                           "graph_us_per_step": round(fused_graph_us, 1),
+                           "graph_pipelined_us_per_step": round(fused_graph_pipe_us, 1)}}
 
 
 def workloads_leg(P, B, synth, np, torch, dev, flush, ev, seed, steps, skip) -> dict:

@@ -9,7 +9,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kAssignThreads = 1024;
+constexpr int kAssignThreads = kGreedyThreads;
 
 __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     const int32_t* __restrict__ counts, int E, int R, const int32_t* __restrict__ rep, int maxrep,
@@ -18,7 +18,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
   __shared__ unsigned char ncand[kMaxE];
   __shared__ __align__(16) unsigned short cand[kMaxE * kMaxRep];  // valid candidates, table order
   assign_block(counts, E, R, rep, maxrep, id_order, assign, act, ncand, cand);
-  for (int g = threadIdx.x; g < R; g += blockDim.x) active[g] = act[g];
+  for (int g = threadIdx.x; g < R; g += kAssignThreads) active[g] = act[g];
 }
 
 }  // namespace

@@ -262,10 +262,13 @@ __device__ __forceinline__ void load_slots(const int32_t* __restrict__ row, int 
 // never index out of bounds.
 __device__ __forceinline__ int expert_rank(int e, int E, int R, const int* __restrict__ assign,
                                            const int* __restrict__ rep, int maxrep) {
-  int r;
-  if (assign != nullptr && assign[e] >= 0) r = assign[e];
-  else if (rep != nullptr) r = rep[e * maxrep];
-  else r = e / (E / R);
+  // both loads issued before either is used (the null tests are uniform);
+  // the empty asm takes both values, so the compiler cannot move the second
+  // load under a test of the first and wait for them in turn
+  int a = assign != nullptr ? assign[e] : -1;
+  int p = rep != nullptr ? rep[(size_t)e * maxrep] : e / (E / R);
+  asm volatile("" : "+v"(a), "+v"(p));
+  const int r = a >= 0 ? a : p;
   return r < 0 ? 0 : (r >= R ? R - 1 : r);
 }
 

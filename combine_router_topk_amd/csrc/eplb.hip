@@ -29,16 +29,24 @@ namespace {
 constexpr int kSplitThreads = 256;
 constexpr int kSummaryThreads = 1024;
 
-// The j-th valid replica of expert e (entries in [0, R), table order), and
-// the number of valid replicas.
-__device__ __forceinline__ int nth_replica(const int32_t* __restrict__ rep, int e, int maxrep, int R,
-                                           int j, int* m_out) {
+// Expert e's replica row in registers, every slot's load issued before any
+// is used (the test on the slot is uniform); slots past maxrep hold -1.
+__device__ __forceinline__ void rep_row(const int32_t* __restrict__ rep, int e, int maxrep,
+                                        int (&x)[kMaxK]) {
+  const int32_t* row = rep + (size_t)e * maxrep;
+#pragma unroll
+  for (int s = 0; s < kMaxK; ++s) x[s] = s < maxrep ? row[s] : -1;
+}
+
+// The j-th valid replica (entries in [0, R), table order) of a row in
+// registers, -1 if there is none, and the number of valid replicas.
+__device__ __forceinline__ int nth_replica(const int (&x)[kMaxK], int R, int j, int* m_out) {
   int m = 0, g_j = -1;
-  for (int s = 0; s < maxrep; ++s) {
-    const int g = rep[e * maxrep + s];
-    if (g < 0 || g >= R) continue;
-    if (m == j) g_j = g;
-    ++m;
+#pragma unroll
+  for (int s = 0; s < kMaxK; ++s) {
+    const bool ok = x[s] >= 0 && x[s] < R;
+    if (ok && m == j) g_j = x[s];
+    m += ok ? 1 : 0;
   }
   *m_out = m;
   return g_j;
@@ -61,21 +69,27 @@ __global__ __launch_bounds__(kSplitThreads) void split_pairs_kernel(
   const int i = blockIdx.x * kSplitThreads + threadIdx.x;
   if (i >= n_pairs) return;
   int e = idx[i];
+  int p = pos[i];
+  asm volatile("" : "+v"(p));  // p's load stays beside idx's, not under the tests below
   e = e < 0 ? 0 : (e >= E ? E - 1 : e);
   const int n = counts[e];
   if (rep == nullptr) {
     gpu_of_pair[i] = e / (E / R);
     return;
   }
+  int off = expert_offsets[e];
+  int x[kMaxK];
+  rep_row(rep, e, maxrep, x);
+  asm volatile("" : "+v"(off));  // off's load stays beside counts' and the row's
   int m = 0;
-  (void)nth_replica(rep, e, maxrep, R, -1, &m);
+  (void)nth_replica(x, R, -1, &m);
   if (m == 0 || n <= 0) {
     gpu_of_pair[i] = -1;  // no valid replica (or inconsistent counts)
     return;
   }
-  const int j = share_index(pos[i] - expert_offsets[e], n, m);
+  const int j = share_index(p - off, n, m);
   int m2 = 0;
-  gpu_of_pair[i] = nth_replica(rep, e, maxrep, R, j, &m2);
+  gpu_of_pair[i] = nth_replica(x, R, j, &m2);
 }
 
 __global__ __launch_bounds__(kSummaryThreads) void split_summary_kernel(
@@ -83,38 +97,44 @@ __global__ __launch_bounds__(kSummaryThreads) void split_summary_kernel(
     int32_t* __restrict__ active, int32_t* __restrict__ tokens) {
   __shared__ int s_act[kMaxR];
   __shared__ int s_tok[kMaxR];
-  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+  for (int r = threadIdx.x; r < R; r += kSummaryThreads) {
     s_act[r] = 0;
     s_tok[r] = 0;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  for (int e = threadIdx.x; e < E; e += kSummaryThreads) {
     const int n = counts[e];
-    if (n <= 0) continue;
-    if (rep == nullptr) {
-      const int g = e / (E / R);
-      atomicAdd(&s_act[g], 1);
-      atomicAdd(&s_tok[g], n);
+    if (rep == nullptr) {  // uniform
+      if (n > 0) {
+        const int g = e / (E / R);
+        atomicAdd(&s_act[g], 1);
+        atomicAdd(&s_tok[g], n);
+      }
       continue;
     }
+    int x[kMaxK];
+    rep_row(rep, e, maxrep, x);
     int m = 0;
-    (void)nth_replica(rep, e, maxrep, R, -1, &m);
-    if (m == 0) continue;
-    const int q = n / m, rem = n % m;
+    (void)nth_replica(x, R, -1, &m);
+    // shares over the valid replicas in table order; a slot adds 0 when it
+    // is not a valid replica, its share is empty or the expert has no pairs
+    // (no test on n before the row is used, so its loads stay beside n's)
+    const int mm = m > 0 ? m : 1;
+    const int q = n / mm, rem = n % mm;
     int j = 0;
     for (int s = 0; s < maxrep; ++s) {
-      const int g = rep[e * maxrep + s];
-      if (g < 0 || g >= R) continue;
+      const int g = x[s < kMaxK ? s : kMaxK - 1];
+      const bool ok = g >= 0 && g < R;
       const int share = q + (j < rem ? 1 : 0);
-      if (share > 0) {
-        atomicAdd(&s_act[g], 1);
-        atomicAdd(&s_tok[g], share);
-      }
-      ++j;
+      const bool on = ok && n > 0 && share > 0;
+      const int gc = ok ? g : 0;
+      atomicAdd(&s_act[gc], on ? 1 : 0);
+      atomicAdd(&s_tok[gc], on ? share : 0);
+      j += ok ? 1 : 0;
     }
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+  for (int r = threadIdx.x; r < R; r += kSummaryThreads) {
     active[r] = s_act[r];
     tokens[r] = s_tok[r];
   }

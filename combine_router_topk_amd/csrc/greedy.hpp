@@ -25,6 +25,8 @@
 namespace moe {
 
 constexpr int kMaxRep = 16;  // replica-table columns (the C ABI caps maxrep)
+constexpr int kGreedyThreads = 1024;  // the workgroup of assign_block
+
 
 // The sequential part of the greedy, run by one wave. Multi-candidate experts
 // are visited in ascending (candidates, id) (or ascending id): each 64-expert
@@ -89,6 +91,65 @@ __device__ __forceinline__ void greedy_walk(int E, int maxrep, int id_order, con
   if (IN_REG && ((gpus >> lane) & 1ull)) act[lane] = static_cast<int>(key_reg >> 16);
 }
 
+// The walk of greedy_walk<true> (at most 64 GPUs) for tables of at most
+// kPackedRep columns, with each expert's valid candidates packed in one
+// 32-bit word: candidate q in bits 6q..6q+5, their number in bits 24..31
+// (0 for an inactive expert). Every 64-expert chunk of words is loaded into
+// registers before the walk, so a choice is one readlane of its expert's
+// word and one readlane of a key per candidate, with no LDS access; the
+// choices of a chunk are gathered in a register and stored once. Same
+// visiting order, same choices and the same `gpus` filter as greedy_walk.
+constexpr int kPackedRep = 4;
+
+__device__ __forceinline__ void greedy_walk_packed(int E, int maxrep, int id_order,
+                                                   const uint32_t* word, int* act,
+                                                   int32_t* __restrict__ assign, uint64_t gpus) {
+  constexpr int kChunks = kMaxE / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nch = (E + kWave - 1) / kWave;
+  uint32_t key_reg = (static_cast<uint32_t>(act[lane]) << 16) | static_cast<uint32_t>(lane);
+  uint32_t wv[kChunks];
+#pragma unroll
+  for (int ch = 0; ch < kChunks; ++ch) {
+    const int e = ch * kWave + lane;
+    wv[ch] = ch < nch ? word[e < E ? e : E - 1] : 0u;  // uniform test; clamped index
+    wv[ch] = e < E ? wv[ch] : 0u;
+  }
+  const int c_lo = id_order ? 0 : 2;  // class 0: any active expert
+  const int c_hi = id_order ? 0 : maxrep;
+  for (int c = c_lo; c <= c_hi; ++c) {
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) {
+      if (ch >= nch) break;
+      const uint32_t wd = wv[ch];
+      const int ce = static_cast<int>(wd >> 24);
+      const uint64_t walked = ballot((c == 0 ? ce > 0 : ce == c) && ((gpus >> (wd & 63u)) & 1ull));
+      uint64_t m = walked;
+      int gsel = -1;
+      while (m != 0ull) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1ull;
+        const uint32_t x = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wd), b));
+        const int n = static_cast<int>(x >> 24);
+        auto key = [&](int q) {
+          return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key_reg), (x >> (6 * q)) & 63u));
+        };
+        uint32_t best = key(0);
+#pragma unroll
+        for (int q = 1; q < kPackedRep; ++q) {
+          const uint32_t kq = key(q);
+          best = (q < n && kq < best) ? kq : best;
+        }
+        const int g = static_cast<int>(best & 0xFFFFu);
+        key_reg += (lane == g) ? 0x10000u : 0u;
+        gsel = (lane == b) ? g : gsel;
+      }
+      if ((walked >> lane) & 1ull) assign[ch * kWave + lane] = gsel;
+    }
+  }
+  if ((gpus >> lane) & 1ull) act[lane] = static_cast<int>(key_reg >> 16);
+}
+
 // The components of the GPU graph in which two GPUs are joined when some
 // walked expert has both as candidates, found by one wave (R <= 64, lane g
 // for GPU g): adj is each GPU's union of the candidate sets of the walked
@@ -125,25 +186,30 @@ __device__ __forceinline__ void assign_block(const int32_t* counts, int E, int R
                                     int32_t* assign, int* act, unsigned char* ncand,
                                     unsigned short* cand) {
   const int tid = threadIdx.x;
-  for (int g = tid; g < (R > kWave ? R : kWave); g += blockDim.x) act[g] = 0;
+  for (int g = tid; g < (R > kWave ? R : kWave); g += kGreedyThreads) act[g] = 0;
   __syncthreads();
   if (rep == nullptr) {
     const int per = E / R;
-    for (int e = tid; e < E; e += blockDim.x) {
+    for (int e = tid; e < E; e += kGreedyThreads) {
       const bool on = counts[e] > 0;
       assign[e] = on ? e / per : -1;
       if (on) atomicAdd(&act[e / per], 1);
     }
   } else {
     // in parallel: each active expert's valid candidates go to LDS, so the
-    // sequential walk below never waits on global memory
-    for (int e = tid; e < E; e += blockDim.x) {
+    // sequential walk below never waits on global memory (the count and the
+    // replica row are loaded together)
+    for (int e = tid; e < E; e += kGreedyThreads) {
+      const int cnt = counts[e];
+      const int32_t* row = rep + (size_t)e * maxrep;
+      int x[kMaxRep];
+#pragma unroll
+      for (int s = 0; s < kMaxRep; ++s) x[s] = s < maxrep ? row[s] : -1;  // uniform test
       int c = 0;
-      if (counts[e] > 0) {
-        for (int s = 0; s < maxrep; ++s) {
-          const int x = rep[e * maxrep + s];
-          if (x >= 0 && x < R) cand[e * kMaxRep + c++] = static_cast<unsigned short>(x);
-        }
+      if (cnt > 0) {
+#pragma unroll
+        for (int s = 0; s < kMaxRep; ++s)
+          if (s < maxrep && x[s] >= 0 && x[s] < R) cand[e * kMaxRep + c++] = static_cast<unsigned short>(x[s]);
       }
       ncand[e] = static_cast<unsigned char>(c);
       if (c == 0) assign[e] = -1;  // inactive (or no valid candidate)

@@ -13,6 +13,7 @@ namespace moe {
 struct Blocking {
   int route_tpb;          // tokens per route block
   int route_nblk;         // route blocks (<= 512)
+  int route_threads;      // threads per route block (1024, or 256 for a small batch)
   int layout_tpb;         // tokens per layout block
   int layout_nblk;        // layout blocks (<= 32 * waves per column task, <= 256)
 };
@@ -41,8 +42,9 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
                         int32_t* counts, int32_t* ws, hipStream_t s);
 
 // The top-k kernel of launch_route alone: idx, w, and one histogram row per
-// route block in ws ([blocking_for(T, E, R).route_nblk, E]), no counts.
-// With ded_rows (R | E, contiguous partition), also one row per route block
+// route block in ws ([blocking_for(T, E, R).route_nblk, E]; none when ws is
+// null), no counts.
+// With ded_rows (and ws; R | E, contiguous partition), also one row per route block
 // of per-rank token counts ([route_nblk, R]: tokens of the block with at
 // least one selected expert on the rank).
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,

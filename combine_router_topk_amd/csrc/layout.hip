@@ -35,8 +35,10 @@
 // The one-call route + assignment + layout (launch_route_assign_layout)
 // picks, after the top-k kernel:
 //  - a decode-sized batch (T <= 1024, T k <= 8192): route_plan_mask_kernel,
-//    one workgroup with one round trip to global memory, the pairs' places
-//    from per-expert token bitmasks counted while the greedy walks;
+//    one workgroup with one round trip to global memory, the demand vector
+//    and the pairs' places from per-expert token bitmasks (the top-k kernel
+//    then writes no histogram rows), the places counted while the greedy
+//    walks;
 //  - a batch of up to 8192 pairs whose tables fit: route_plan_small_kernel;
 //  - a larger batch without a replica table: plan_scan_kernel and
 //    layout_permute_scan_kernel, from the top-k kernel's per-block expert
@@ -61,13 +63,23 @@ __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (
 // token, its distinct destination ranks (s_ded); with lead_mask, bit j of
 // lead_mask[t] marks slot j as the token's first slot on its rank. All
 // threads of the block take part.
+template <int NT>
 __device__ __forceinline__ void count_tokens(const int32_t* __restrict__ idx, int t0, int t1, int E, int k,
                              const int* s_rank, int* s_hist, int* s_ded,
                              int32_t* __restrict__ lead_mask) {
   const size_t i0 = (size_t)t0 * k, i1 = (size_t)t1 * k;
-  for (size_t i = i0 + threadIdx.x; i < i1; i += blockDim.x)
-    atomicAdd(&s_hist[clamp_expert(idx[i], E)], 1);
-  for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
+  const size_t nt = NT;
+  // four loads in flight at a time: clamped indices, and an add of 0 for a
+  // slot past the end (a value used only under a condition has its load
+  // moved under that condition, and waited for on its own)
+  for (size_t i = i0 + threadIdx.x; i < i1; i += 4 * nt) {
+    int v[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[b] = idx[i + b * nt < i1 ? i + b * nt : i1 - 1];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) atomicAdd(&s_hist[clamp_expert(v[b], E)], i + b * nt < i1 ? 1 : 0);
+  }
+  for (int t = t0 + threadIdx.x; t < t1; t += NT) {
     // ranks of the token's k experts in registers, then one count per
     // distinct rank (the first slot that reaches it)
     int ids[kMaxK];
@@ -98,17 +110,17 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
   int* s_rank = smem;        // [E]
   int* s_hist = smem + E;    // [E]
   int* s_ded = smem + 2 * E; // [R]
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  for (int e = threadIdx.x; e < E; e += kCountThreads) {
     s_rank[e] = expert_rank(e, E, R, assign, rep, maxrep);
     s_hist[e] = 0;
   }
-  for (int r = threadIdx.x; r < R; r += blockDim.x) s_ded[r] = 0;
+  for (int r = threadIdx.x; r < R; r += kCountThreads) s_ded[r] = 0;
   __syncthreads();
   const int t0 = blockIdx.x * tpb;
-  count_tokens(idx, t0, min(T, t0 + tpb), E, k, s_rank, s_hist, s_ded, lead_mask);
+  count_tokens<kCountThreads>(idx, t0, min(T, t0 + tpb), E, k, s_rank, s_hist, s_ded, lead_mask);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = s_hist[e];
-  for (int r = threadIdx.x; r < R; r += blockDim.x) ded[(size_t)blockIdx.x * R + r] = s_ded[r];
+  for (int e = threadIdx.x; e < E; e += kCountThreads) hist[(size_t)blockIdx.x * E + e] = s_hist[e];
+  for (int r = threadIdx.x; r < R; r += kCountThreads) ded[(size_t)blockIdx.x * R + r] = s_ded[r];
 }
 
 // Column pass over the two per-block matrices: hist [rows, E] and ded
@@ -347,7 +359,7 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_permute_kernel(
   int* wcnt = smem + E;              // [WAVES][E] pairs per expert in a wave
   int* wtag = smem + E + WAVES * E;  // [WAVES][E] round that wrote wcnt
   const int b = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  for (int e = threadIdx.x; e < E; e += WAVES * kWave) {
     run[e] = expert_offsets[e] + base[(size_t)b * E + e];
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) wtag[w * E + e] = 0;
@@ -432,7 +444,7 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_permute_ss_kernel(
     int* run = smem;                   // [E] next free row of each expert
     int* wcnt = smem + E;              // [WAVES][E]
     int* wtag = smem + E + WAVES * E;  // [WAVES][E]
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    for (int e = threadIdx.x; e < E; e += WAVES * kWave) {
       run[e] = expert_offsets[e] + base[(size_t)b * E + e];
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) wtag[w * E + e] = 0;
@@ -444,8 +456,8 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_permute_ss_kernel(
   int* run = smem + E;                      // [R] next free single-send row of each rank
   int* wcnt = smem + E + R;                 // [WAVES][R]
   int* wtag = smem + E + R + WAVES * R;     // [WAVES][R]
-  for (int e = threadIdx.x; e < E; e += blockDim.x) s_rank[e] = rank_of[e];
-  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+  for (int e = threadIdx.x; e < E; e += WAVES * kWave) s_rank[e] = rank_of[e];
+  for (int r = threadIdx.x; r < R; r += WAVES * kWave) {
     run[r] = ss_rank_offsets[r] + ss_base[(size_t)b * R + r];
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) wtag[w * R + r] = 0;
@@ -489,25 +501,25 @@ __device__ __forceinline__ void layout_small_block(
   int* wcnt = run + M;           // [16][M]
   int* wtag = wcnt + kPlanWaves * M;  // [16][M]
   const bool ss = ss_rank_offsets != nullptr;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  for (int e = threadIdx.x; e < E; e += kPlanThreads) {
     s_rank[e] = expert_rank(e, E, R, assign, rep, maxrep);
     s_cnt[e] = 0;
   }
-  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+  for (int r = threadIdx.x; r < R; r += kPlanThreads) {
     s_ded[r] = 0;
     s_rtok[r] = 0;
   }
   __syncthreads();
-  count_tokens(idx, 0, T, E, k, s_rank, s_cnt, s_ded, ss ? lead : nullptr);
+  count_tokens<kPlanThreads>(idx, 0, T, E, k, s_rank, s_cnt, s_ded, ss ? lead : nullptr);
   __syncthreads();
   plan_finish(E, R, s_rank, s_cnt, s_ded, s_rtok, s_roff, s_wave, s_wave2, rank_of,
               expert_offsets, rank_offsets, dedup, ss_rank_offsets, run, s_ssoff);
-  for (int i = threadIdx.x; i < kPlanWaves * E; i += blockDim.x) wtag[i] = 0;
+  for (int i = threadIdx.x; i < kPlanWaves * E; i += kPlanThreads) wtag[i] = 0;
   __syncthreads();
   permute_rounds<kPlanWaves>(idx, 0, (int64_t)T * k, E, T * k, run, wcnt, wtag, pos, src);
   if (!ss) return;  // uniform: a kernel argument
-  for (int r = threadIdx.x; r < R; r += blockDim.x) run[r] = s_ssoff[r];
-  for (int i = threadIdx.x; i < kPlanWaves * R; i += blockDim.x) wtag[i] = 0;
+  for (int r = threadIdx.x; r < R; r += kPlanThreads) run[r] = s_ssoff[r];
+  for (int i = threadIdx.x; i < kPlanWaves * R; i += kPlanThreads) wtag[i] = 0;
   __syncthreads();
   single_send_rounds<kPlanWaves>(idx, 0, (int64_t)T * k, k, E, R, T * k, s_rank, run, wcnt, wtag,
                                  lead, ss_row, ss_token);
@@ -562,26 +574,33 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_small_kernel(
   const int tid = threadIdx.x;
   // demand vector: column sums of the [nblk, E] histogram rows, the rows
   // split among max(1, 1024 / E) thread groups per column (integer adds)
-  for (int e = tid; e < E; e += blockDim.x) s_counts[e] = 0;
+  for (int e = tid; e < E; e += kPlanThreads) s_counts[e] = 0;
   __syncthreads();
   {
     const int groups = E >= kPlanThreads ? 1 : kPlanThreads / E;
     const int g = tid / E;
     for (int e = tid % E; g < groups && e < E; e += kPlanThreads) {
+      // sixteen rows' loads in flight at a time (clamped rows, masked after)
       int acc = 0;
-      for (int r = g; r < nblk; r += groups) acc += hist[(size_t)r * E + e];
+      for (int r0 = g; r0 < nblk; r0 += 16 * groups) {
+        int v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = hist[(size_t)min(r0 + i * groups, nblk - 1) * E + e];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc += r0 + i * groups < nblk ? v[i] : 0;
+      }
       atomicAdd(&s_counts[e], acc);
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) counts[e] = s_counts[e];
+  for (int e = tid; e < E; e += kPlanThreads) counts[e] = s_counts[e];
   // greedy replica assignment into LDS
   int* act = region;
   unsigned char* ncand = reinterpret_cast<unsigned char*>(region + (R > kWave ? R : kWave));
   unsigned short* cand = reinterpret_cast<unsigned short*>(region + (R > kWave ? R : kWave) + (E + 3) / 4);
   assign_block(s_counts, E, R, rep, maxrep, id_order, s_assign, act, ncand, cand);
-  for (int e = tid; e < E; e += blockDim.x) assign[e] = s_assign[e];
-  for (int g = tid; g < R; g += blockDim.x) active[g] = act[g];
+  for (int e = tid; e < E; e += kPlanThreads) assign[e] = s_assign[e];
+  for (int g = tid; g < R; g += kPlanThreads) active[g] = act[g];
   __syncthreads();  // the region is reused below
   layout_small_block(idx, T, E, k, R, s_assign, rep, maxrep, rank_of, expert_offsets, rank_offsets,
                      pos, src, dedup, nullptr, nullptr, nullptr, nullptr, region, s_wave, s_wave2);
@@ -723,16 +742,18 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_permute_scan_kernel(
 
 // The routing plan of a decode-sized batch (T <= 1024 tokens, T k <= 8192
 // pairs) after the top-k kernel, in one workgroup with one round trip to
-// global memory: the route's histogram rows, the expert ids and the replica
-// rows are all loaded at the start. A pair's place inside its expert's
-// segment does not depend on the assignment, so it is computed while the
-// greedy walks: each expert gets a bitmask of the tokens that chose it, and
-// the place of pair (t, e) is the number of bits of e's mask below t (a token
-// chooses an expert at most once, so this is the stable rank). Wave 0 walks
-// the multi-copy experts in order (greedy_walk) while waves 1..15 count
-// those bits. Then the ranks of the experts, the per-token dedup counts and
-// the offsets (finish_few_ranks for up to 64 ranks, else plan_finish), and
-// pos = expert offset + place.
+// global memory: the expert ids and the replica rows are loaded at the
+// start. Each expert gets a bitmask of the tokens that chose it; its count
+// is the number of bits set (a token chooses an expert at most once), and
+// the place of pair (t, e) inside e's segment is the number of bits of e's
+// mask below t, the stable rank. The places do not depend on the
+// assignment, so they are computed while the greedy walks. The walkers
+// (waves 0..3, one per component group of the GPU graph, with at most 64
+// GPUs; else wave 0) visit the multi-copy experts in order (greedy_walk, or
+// greedy_walk_packed for tables of at most 4 columns) while the other waves
+// count those bits. Then the ranks of the experts, the per-token dedup
+// counts and the offsets (finish_few_ranks for up to 64 ranks, else
+// plan_finish), and pos = expert offset + place.
 // Outputs equal those of route_plan_small_kernel.
 constexpr int kMaskMaxT = 1024;
 constexpr int kMaskPairsPerThread = kSmallPairs / kPlanThreads;
@@ -828,7 +849,7 @@ __device__ __forceinline__ void finish_few_ranks(
 }
 
 __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
-    const int32_t* __restrict__ hist, int nblk, const int32_t* __restrict__ idx, int T, int E,
+    const int32_t* __restrict__ idx, int T, int E,
     int k, int R, const int32_t* __restrict__ rep, int maxrep, int id_order,
     int32_t* __restrict__ counts, int32_t* __restrict__ assign, int32_t* __restrict__ active,
     int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
@@ -853,46 +874,41 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
   int* s_roff = p;   p += round4(R);
   int* act = p;      p += round4(R > kWave ? R : kWave);
   unsigned char* ncand = reinterpret_cast<unsigned char*>(p); p += round4((E + 3) / 4);
-  unsigned short* cand = reinterpret_cast<unsigned short*>(p); p += round4(E * kMaxRep / 2);
+  unsigned short* cand = reinterpret_cast<unsigned short*>(p);
+  uint32_t* word = reinterpret_cast<uint32_t*>(p); p += round4(E * kMaxRep / 2);  // cand or word [E]
   unsigned short* s_idx = reinterpret_cast<unsigned short*>(p); p += round4((n + 1) / 2);
   unsigned short* s_rk = reinterpret_cast<unsigned short*>(p); p += round4((n + 1) / 2);
   const bool few = R <= kWave;  // the ballot-based end (finish_few_ranks)
+  // the packed walk: at most 64 GPUs and kPackedRep table columns
+  const bool packed = few && rep != nullptr && maxrep <= kPackedRep;
   int* s_wr = p;    p += few ? round4(kPlanWaves * R) : 0;
   int* s_rbase = p; p += few ? round4(R + 1) : 0;
   int* s_ord = p;   p += few ? round4(E) : 0;
   int* s_scan = p;  p += few ? round4(E) : 0;
   unsigned long long* adj = reinterpret_cast<unsigned long long*>(p);  // [64] when few
 
-  // every global load first: histogram column partials (eight rows per
-  // thread issued together, a loop for any further rows), expert ids,
-  // replica rows
-  const int groups = E >= kPlanThreads ? 1 : kPlanThreads / E;
-  const int col = tid % E, grp = tid / E;
-  int part = 0;
-  if (grp < groups) {
-    int v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = grp + i * groups;
-      v[i] = r < nblk ? hist[(size_t)r * E + col] : 0;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) part += v[i];
-    for (int r = grp + 8 * groups; r < nblk; r += groups) part += hist[(size_t)r * E + col];
-  }
+  // every global load first, all in flight together: expert ids and replica
+  // rows. Each load reads an index clamped into its array (T, k, maxrep >= 1
+  // here) and is masked afterwards: a load under its own condition is
+  // waited for before the next one is issued.
   int pe[kMaskPairsPerThread];
 #pragma unroll
-  for (int j = 0; j < kMaskPairsPerThread; ++j) {
-    const int i = tid + j * kPlanThreads;
-    pe[j] = i < n ? clamp_expert(idx[i], E) : 0;
-  }
+  for (int j = 0; j < kMaskPairsPerThread; ++j) pe[j] = idx[min(tid + j * kPlanThreads, n - 1)];
   int rr[kMaxRep];
+  {
+    const int32_t* row = rep + (size_t)min(tid, E - 1) * maxrep;  // read only with a table
+#pragma unroll
+    for (int s = 0; s < kMaxRep; ++s) rr[s] = (rep != nullptr && s < maxrep) ? row[s] : -1;  // uniform
+  }
+#pragma unroll
+  for (int j = 0; j < kMaskPairsPerThread; ++j)
+    pe[j] = tid + j * kPlanThreads < n ? clamp_expert(pe[j], E) : 0;
 #pragma unroll
   for (int s = 0; s < kMaxRep; ++s)
-    rr[s] = (rep != nullptr && tid < E && s < maxrep) ? rep[tid * maxrep + s] : -1;
+    rr[s] = (rep != nullptr && tid < E && s < maxrep) ? rr[s] : -1;
 
   for (int i = tid; i < W * E; i += kPlanThreads) mask[i] = 0ull;
-  for (int i = tid; i < e8; i += kPlanThreads) s_counts[i] = 0;
+  for (int i = E + tid; i < e8; i += kPlanThreads) s_counts[i] = 0;  // the padding
   for (int i = tid; i < R; i += kPlanThreads) {
     s_ded[i] = 0;
     s_rtok[i] = 0;
@@ -903,7 +919,6 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
     if (tid < kWave) adj[tid] = 0ull;
   }
   __syncthreads();
-  if (grp < groups && part != 0) atomicAdd(&s_counts[col], part);
 #pragma unroll
   for (int j = 0; j < kMaskPairsPerThread; ++j) {
     const int i = tid + j * kPlanThreads;
@@ -914,33 +929,57 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
     }
   }
   __syncthreads();
-  // active experts: their valid candidates to LDS; single-copy experts (and
-  // every expert without a table) are placed at once
+  // the demand vector: an expert's count is the number of bits of its mask
+  // (a token selects an expert at most once); active experts' valid
+  // candidates to LDS; single-copy experts (and every expert without a
+  // table) are placed at once
   if (tid < E) {
-    const int c = s_counts[tid];
+    unsigned long long mw[kMaskMaxT / 64];
+#pragma unroll
+    for (int q = 0; q < kMaskMaxT / 64; ++q) mw[q] = q < W ? mask[tid * W + q] : 0ull;  // uniform test
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < kMaskMaxT / 64; ++q) c += __popcll(mw[q]);
+    s_counts[tid] = c;
     counts[tid] = c;
     if (rep == nullptr) {
       const int per = E / R;
       s_assign[tid] = c > 0 ? tid / per : -1;
       if (c > 0) atomicAdd(&act[tid / per], 1);
     } else {
-      int nc = 0;
+      // the valid candidates, from the replica row in registers: packed in
+      // one word (packed walk) or listed in cand
+      int nc = 0, g0 = 0;
+      uint32_t wd = 0u;
+      unsigned long long cm = 0ull;
       if (c > 0) {
 #pragma unroll
-        for (int s = 0; s < kMaxRep; ++s)
-          if (rr[s] >= 0 && rr[s] < R) cand[tid * kMaxRep + nc++] = static_cast<unsigned short>(rr[s]);
+        for (int s = 0; s < kMaxRep; ++s) {
+          if (s >= maxrep) break;  // uniform
+          const int g = rr[s];
+          if (g >= 0 && g < R) {
+            g0 = nc == 0 ? g : g0;
+            if (packed) wd |= static_cast<uint32_t>(g) << (6 * nc);
+            else cand[tid * kMaxRep + nc] = static_cast<unsigned short>(g);
+            cm |= 1ull << (g & 63);
+            ++nc;
+          }
+        }
       }
-      ncand[tid] = static_cast<unsigned char>(nc);
+      if (packed) word[tid] = wd | (static_cast<uint32_t>(nc) << 24);
+      else ncand[tid] = static_cast<unsigned char>(nc);
       if (nc == 0) s_assign[tid] = -1;
       if (!id_order && nc == 1) {
-        s_assign[tid] = cand[tid * kMaxRep];
-        atomicAdd(&act[cand[tid * kMaxRep]], 1);
+        s_assign[tid] = g0;
+        atomicAdd(&act[g0], 1);
       }
       // the GPU graph of the walked experts: each candidate learns the others
       if (few && nc >= (id_order ? 1 : 2)) {
-        unsigned long long cm = 0ull;
-        for (int q = 0; q < nc; ++q) cm |= 1ull << cand[tid * kMaxRep + q];
-        for (int q = 0; q < nc; ++q) atomicOr(&adj[cand[tid * kMaxRep + q]], cm);
+#pragma unroll
+        for (int s = 0; s < kMaxRep; ++s) {
+          if (s >= maxrep) break;  // uniform
+          if (rr[s] >= 0 && rr[s] < R) atomicOr(&adj[rr[s]], cm);
+        }
       }
     }
   }
@@ -953,7 +992,10 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
     if (rep != nullptr) {
       if (few) {
         const uint64_t gpus = walker_gpus(adj, R, wave, walkers);
-        if (gpus != 0ull) greedy_walk<true>(E, maxrep, id_order, ncand, cand, act, s_assign, gpus);
+        if (gpus != 0ull) {
+          if (packed) greedy_walk_packed(E, maxrep, id_order, word, act, s_assign, gpus);
+          else greedy_walk<true>(E, maxrep, id_order, ncand, cand, act, s_assign, gpus);
+        }
       } else {
         greedy_walk<false>(E, maxrep, id_order, ncand, cand, act, s_assign);
       }
@@ -969,9 +1011,11 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
     }
   }
   __syncthreads();
-  if (tid < E) {
-    assign[tid] = s_assign[tid];
-    s_rank[tid] = expert_rank(tid, E, R, s_assign, rep, maxrep);
+  if (tid < E) {  // an expert's rank: its assignment, else its first-listed copy (in rr[0])
+    const int a = s_assign[tid];
+    assign[tid] = a;
+    const int r = a >= 0 ? a : (rep != nullptr ? rr[0] : tid / (E / R));
+    s_rank[tid] = r < 0 ? 0 : (r >= R ? R - 1 : r);
   }
   for (int g = tid; g < R; g += kPlanThreads) active[g] = act[g];
   __syncthreads();
@@ -1073,10 +1117,11 @@ hipError_t launch_route_assign_layout(const float* logits, int T, int E, int k, 
   const size_t plan_ints = plan_small_ints(E, R);
   if (T > 0 && T <= kMaskMaxT && (int64_t)T * k <= kSmallPairs &&
       mask_plan_ints(T, E, k, R) <= kSmallLdsInts) {
-    hipError_t err = launch_route_topk(logits, T, E, k, idx, w, ws, s);
+    // the plan counts the experts from idx itself: no histogram rows
+    hipError_t err = launch_route_topk(logits, T, E, k, idx, w, nullptr, s);
     if (err != hipSuccess) return err;
     route_plan_mask_kernel<<<1, kPlanThreads, mask_plan_ints(T, E, k, R) * sizeof(int), s>>>(
-        ws, blocking_for(T, E, R).route_nblk, idx, T, E, k, R, rep, rep ? maxrep : 1,
+        idx, T, E, k, R, rep, rep ? maxrep : 1,
         id_order ? 1 : 0, counts, assign, active, rank_of, expert_offsets, rank_offsets, pos, src,
         dedup);
     return hipGetLastError();

@@ -28,28 +28,24 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 1024;
+constexpr int kRouteThreadsSmall = 256;  // small batches (see blocking_for)
 constexpr int kRouteTargetBlocks = 512;
 
 // With ded_rows set (contiguous partition, per = E / R experts per rank),
 // each block also counts, per rank, its tokens with at least one selected
 // expert on that rank (the single-send counts), written as one row of a
 // [blocks, R] matrix beside the expert histogram.
-template <int L, int V>
-__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
+template <int L, int V, int NT>
+__global__ __launch_bounds__(NT) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int tpb, int32_t* __restrict__ idx,
     float* __restrict__ w, int32_t* __restrict__ block_hist, int32_t* __restrict__ ded_rows, int R,
     int per) {
   extern __shared__ int s_hist[];
   int* s_ded = s_hist + E;  // [R], used with ded_rows
-  for (int e = threadIdx.x; e < E; e += blockDim.x) s_hist[e] = 0;
-  if (ded_rows != nullptr)
-    for (int r = threadIdx.x; r < R; r += blockDim.x) s_ded[r] = 0;
-  __syncthreads();
-
   constexpr int TPW = kWave / L;  // tokens per wave step
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int nwaves = blockDim.x / kWave;
+  const int nwaves = NT / kWave;
   const int grp = lane / L;
   const int sl = lane % L;
   const uint64_t gmask = (L == 64) ? ~0ull : ((1ull << L) - 1ull) << (grp * L);
@@ -68,6 +64,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
       nxt[v] = (t < t_end && e < E) ? logits[(size_t)t * E + e] : 0.0f;
     }
   }
+  if (block_hist != nullptr)  // uniform: a kernel argument
+    for (int e = threadIdx.x; e < E; e += NT) s_hist[e] = 0;  // loads in flight meanwhile
+  if (ded_rows != nullptr)
+    for (int r = threadIdx.x; r < R; r += NT) s_ded[r] = 0;
+  __syncthreads();
   for (int t0 = t_begin + wave * TPW; t0 < t_end; t0 += tstep) {
     const int t = t0 + grp;
     const bool valid = t < t_end;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
       const size_t o = (size_t)t * k + sl;
       idx[o] = my_e;
       w[o] = static_cast<float>(ex / sum);
-      atomicAdd(&s_hist[my_e], 1);
+      if (block_hist != nullptr) atomicAdd(&s_hist[my_e], 1);
     }
     if (ded_rows != nullptr) {  // uniform: a kernel argument
       // a slot counts for its rank unless a lower slot of the token has it
@@ -136,11 +137,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     }
   }
   __syncthreads();
-  int32_t* row = block_hist + (size_t)blockIdx.x * E;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) row[e] = s_hist[e];
+  if (block_hist != nullptr) {
+    int32_t* row = block_hist + (size_t)blockIdx.x * E;
+    for (int e = threadIdx.x; e < E; e += NT) row[e] = s_hist[e];
+  }
   if (ded_rows != nullptr) {
     int32_t* drow = ded_rows + (size_t)blockIdx.x * R;
-    for (int r = threadIdx.x; r < R; r += blockDim.x) drow[r] = s_ded[r];
+    for (int r = threadIdx.x; r < R; r += NT) drow[r] = s_ded[r];
   }
 }
 
@@ -157,21 +160,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 // s KP + j, and one fp64 pass evaluates the whole batch. Evaluated per token,
 // the softmax used k of the 64 lanes for the cost of all.
 // ded_rows, R and per as in route_topk_kernel.
-template <int V, int KP>
-__global__ __launch_bounds__(kRouteThreads) void route_topk_wave_kernel(
+template <int V, int KP, int NT>
+__global__ __launch_bounds__(NT) void route_topk_wave_kernel(
     const float* __restrict__ logits, int T, int E, int k, int tpb, int32_t* __restrict__ idx,
     float* __restrict__ w, int32_t* __restrict__ block_hist, int32_t* __restrict__ ded_rows, int R,
     int per) {
   extern __shared__ int s_hist[];
   int* s_ded = s_hist + E;  // [R], used with ded_rows
-  for (int e = threadIdx.x; e < E; e += blockDim.x) s_hist[e] = 0;
-  if (ded_rows != nullptr)
-    for (int r = threadIdx.x; r < R; r += blockDim.x) s_ded[r] = 0;
-  __syncthreads();
-
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int nwaves = blockDim.x / kWave;
+  const int nwaves = NT / kWave;
   const int e0 = lane * V;
   const bool vec = (E & 3) == 0;  // rows are whole 16-byte chunks
   const int t_begin = blockIdx.x * tpb;
@@ -209,7 +207,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_wave_kernel(
       const size_t o = (size_t)b_t * k + j;
       idx[o] = static_cast<int32_t>(b_e);
       w[o] = static_cast<float>(ex / sum);
-      atomicAdd(&s_hist[b_e], 1);
+      if (block_hist != nullptr) atomicAdd(&s_hist[b_e], 1);
     }
     if (ded_rows != nullptr) {  // uniform: a kernel argument
       // a slot counts for its rank unless a lower slot of the token has it
@@ -226,6 +224,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_wave_kernel(
 
   float nxt[V];
   load_row(t_begin + wave, nxt);
+  if (block_hist != nullptr)  // uniform: a kernel argument
+    for (int e = threadIdx.x; e < E; e += NT) s_hist[e] = 0;  // the load in flight meanwhile
+  if (ded_rows != nullptr)
+    for (int r = threadIdx.x; r < R; r += NT) s_ded[r] = 0;
+  __syncthreads();
   for (int t = t_begin + wave; t < t_end; t += nwaves) {
     uint32_t key[V];
 #pragma unroll
@@ -264,11 +267,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_wave_kernel(
   }
   if (slot > 0) flush(slot);
   __syncthreads();
-  int32_t* row = block_hist + (size_t)blockIdx.x * E;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) row[e] = s_hist[e];
+  if (block_hist != nullptr) {
+    int32_t* row = block_hist + (size_t)blockIdx.x * E;
+    for (int e = threadIdx.x; e < E; e += NT) row[e] = s_hist[e];
+  }
   if (ded_rows != nullptr) {
     int32_t* drow = ded_rows + (size_t)blockIdx.x * R;
-    for (int r = threadIdx.x; r < R; r += blockDim.x) drow[r] = s_ded[r];
+    for (int r = threadIdx.x; r < R; r += NT) drow[r] = s_ded[r];
   }
 }
 
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(1024) void column_sum_kernel(const int32_t* __restr
 
 struct TopkArgs {
   const float* logits;
-  int T, E, k, tpb, nblk;
+  int T, E, k, tpb, nblk, threads;
   int32_t* idx;
   float* w;
   int32_t* hist;
@@ -316,15 +321,19 @@ struct TopkArgs {
 
 template <int L, int V>
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  route_topk_kernel<L, V><<<a.nblk, kRouteThreads, a.lds(), s>>>(a.logits, a.T, a.E, a.k, a.tpb, a.idx,
-                                                                 a.w, a.hist, a.ded, a.R, a.per);
+  if (a.threads == kRouteThreadsSmall)
+    route_topk_kernel<L, V, kRouteThreadsSmall><<<a.nblk, kRouteThreadsSmall, a.lds(), s>>>(
+        a.logits, a.T, a.E, a.k, a.tpb, a.idx, a.w, a.hist, a.ded, a.R, a.per);
+  else
+    route_topk_kernel<L, V, kRouteThreads><<<a.nblk, kRouteThreads, a.lds(), s>>>(
+        a.logits, a.T, a.E, a.k, a.tpb, a.idx, a.w, a.hist, a.ded, a.R, a.per);
   return hipGetLastError();
 }
 
-template <int V>
-hipError_t launch_wave(const TopkArgs& a, hipStream_t s) {
+template <int V, int NT>
+hipError_t launch_wave_nt(const TopkArgs& a, hipStream_t s) {
 #define MOE_WAVE(KP)                                                                    \
-  route_topk_wave_kernel<V, KP><<<a.nblk, kRouteThreads, a.lds(), s>>>(                 \
+  route_topk_wave_kernel<V, KP, NT><<<a.nblk, NT, a.lds(), s>>>(                        \
       a.logits, a.T, a.E, a.k, a.tpb, a.idx, a.w, a.hist, a.ded, a.R, a.per)
   if (a.k <= 1) MOE_WAVE(1);
   else if (a.k <= 2) MOE_WAVE(2);
@@ -333,6 +342,12 @@ hipError_t launch_wave(const TopkArgs& a, hipStream_t s) {
   else MOE_WAVE(16);
 #undef MOE_WAVE
   return hipGetLastError();
+}
+
+template <int V>
+hipError_t launch_wave(const TopkArgs& a, hipStream_t s) {
+  return a.threads == kRouteThreadsSmall ? launch_wave_nt<V, kRouteThreadsSmall>(a, s)
+                                         : launch_wave_nt<V, kRouteThreads>(a, s);
 }
 
 // Lanes per token: about four logits per lane measured fastest (T = 65536,
@@ -350,12 +365,28 @@ int lanes_per_token(int E) {
 Blocking blocking_for(int T, int E, int R) {
   Blocking b{};
   const int tpw = kWave / lanes_per_token(E);
-  const int step = tpw * (kRouteThreads / kWave);
-  int tpb = (T + kRouteTargetBlocks - 1) / kRouteTargetBlocks;
-  tpb = ((tpb + step - 1) / step) * step;
-  if (tpb < step) tpb = step;
-  b.route_tpb = tpb;
-  b.route_nblk = (T + tpb - 1) / tpb;
+  // A small batch takes 256-thread blocks of one token step per wave: the
+  // blocks spread over four times the CUs with one wave per SIMD (in a
+  // 1024-thread block four waves share each SIMD and the block waits for
+  // the last). Only while the one-workgroup plans, which sum the blocks'
+  // histogram rows per column with 1024 / E thread groups, keep at most 16
+  // rows per group (and at most 64 blocks).
+  const int step_small = tpw * (kRouteThreadsSmall / kWave);
+  const int groups = E >= 1024 ? 1 : 1024 / E;
+  const int nblk_small = (T + step_small - 1) / step_small;
+  if (nblk_small <= 64 && nblk_small <= 16 * groups) {
+    b.route_threads = kRouteThreadsSmall;
+    b.route_tpb = step_small;
+    b.route_nblk = nblk_small;
+  } else {
+    const int step = tpw * (kRouteThreads / kWave);
+    int tpb = (T + kRouteTargetBlocks - 1) / kRouteTargetBlocks;
+    tpb = ((tpb + step - 1) / step) * step;
+    if (tpb < step) tpb = step;
+    b.route_threads = kRouteThreads;
+    b.route_tpb = tpb;
+    b.route_nblk = (T + tpb - 1) / tpb;
+  }
   // The layout plan scans [blocks, E] and [blocks, R] in tasks of 64 columns
   // with 16 waves; each wave may own at most 48 rows of one task, so the
   // block count is capped at 48 * (waves per task), and at 256.
@@ -395,7 +426,7 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
   const Blocking b = blocking_for(T, E, 1);
   const int L = lanes_per_token(E);
   const int V = (E + L - 1) / L;  // L = 16: 1..4; 32: 3..4; 64: 3..16
-  const TopkArgs a{logits, T, E, k, b.route_tpb, b.route_nblk, idx, w, ws, ded_rows, R,
+  const TopkArgs a{logits, T, E, k, b.route_tpb, b.route_nblk, b.route_threads, idx, w, ws, ded_rows, R,
                    ded_rows != nullptr ? E / R : 1};
   if (L == 16 && V == 1) return launch_topk<16, 1>(a, s);
   if (L == 16 && V == 2) return launch_topk<16, 2>(a, s);

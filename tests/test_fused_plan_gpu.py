@@ -200,3 +200,23 @@ def test_decode_plan_without_two_copy_experts(order):
     rep[:, 0] = (np.arange(E) * 7) % R
     w = synth.Workload("one_copy_each", 256, E, 4, 8, R, synth.F16, "none", False)
     run_both(w, 8, rep=rep, order=order)
+
+
+@pytest.mark.parametrize("order", ["constrained", "id"])
+def test_decode_plan_four_column_table_with_holes(order):
+    """Rows of four slots holding one to four distinct GPUs, the primary in
+    slot 0 (the table's contract) and the others at random slots among 1..3
+    (-1 in the rest): the decode plan's packed walk at its widest table,
+    experts with four candidates included, against the separate calls and
+    the oracle."""
+    rng = np.random.default_rng(77)
+    E, R, maxrep = 128, 32, 4
+    rep = np.full((E, maxrep), -1, np.int32)
+    for e in range(E):
+        n = int(rng.integers(1, maxrep + 1))
+        gpus = rng.choice(R, size=n, replace=False)
+        rep[e, 0] = gpus[0]
+        rep[e, 1 + rng.choice(maxrep - 1, size=n - 1, replace=False)] = gpus[1:]
+    assert (np.sum(rep >= 0, axis=1) == 4).any()
+    w = synth.Workload("four_columns_holes", 700, E, 8, 8, R, synth.BF16, "zipf1.2", False)
+    run_both(w, 9, rep=rep, order=order)
