@@ -149,6 +149,10 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
   return v;
 }
 
+constexpr int kDppRowShr1 = 0x111;     // lane i <- lane i-1 within a row of 16
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
 constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> every lane of the next row
 constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> every lane of rows 2 and 3
 
@@ -219,13 +223,20 @@ __device__ __forceinline__ double group_sum_f64(double x) {
   return x;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active), in
+// DPP moves rather than LDS permutes: shifts by 1, 2, 4 and 8 lanes inside
+// each row of 16 (a lane shifted in from outside its row reads 0) give the
+// row prefixes; then lane 15's sum is added to row 1 and lane 47's to row 3
+// (row_bcast:15), and lane 31's to rows 2 and 3 (row_bcast:31). `lane` is
+// kept for the callers' convenience.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+  (void)lane;
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
   return v;
 }
 

@@ -98,12 +98,21 @@ __device__ __forceinline__ void greedy_walk(int E, int maxrep, int id_order, con
 // registers before the walk, so a choice is one readlane of its expert's
 // word and one readlane of a key per candidate, with no LDS access; the
 // choices of a chunk are gathered in a register and stored once. Same
-// visiting order, same choices and the same `gpus` filter as greedy_walk.
+// visiting order and same choices as greedy_walk; the walker's GPUs are
+// found with walker_gpus (adj, R, walker, walkers as there) while the
+// words and counters are in flight.
 constexpr int kPackedRep = 4;
 
+__device__ __forceinline__ uint64_t walker_gpus(const unsigned long long* adj, int R, int walker,
+                                                int walkers);
+
+// NC: the most candidates an expert can have (maxrep <= NC <= kPackedRep).
+template <int NC>
 __device__ __forceinline__ void greedy_walk_packed(int E, int maxrep, int id_order,
                                                    const uint32_t* word, int* act,
-                                                   int32_t* __restrict__ assign, uint64_t gpus) {
+                                                   int32_t* __restrict__ assign,
+                                                   const unsigned long long* adj, int R,
+                                                   int walker, int walkers) {
   constexpr int kChunks = kMaxE / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int nch = (E + kWave - 1) / kWave;
@@ -115,6 +124,8 @@ __device__ __forceinline__ void greedy_walk_packed(int E, int maxrep, int id_ord
     wv[ch] = ch < nch ? word[e < E ? e : E - 1] : 0u;  // uniform test; clamped index
     wv[ch] = e < E ? wv[ch] : 0u;
   }
+  const uint64_t gpus = walker_gpus(adj, R, walker, walkers);
+  if (gpus == 0ull) return;  // uniform
   const int c_lo = id_order ? 0 : 2;  // class 0: any active expert
   const int c_hi = id_order ? 0 : maxrep;
   for (int c = c_lo; c <= c_hi; ++c) {
@@ -136,12 +147,15 @@ __device__ __forceinline__ void greedy_walk_packed(int E, int maxrep, int id_ord
         };
         uint32_t best = key(0);
 #pragma unroll
-        for (int q = 1; q < kPackedRep; ++q) {
+        for (int q = 1; q < NC; ++q) {
           const uint32_t kq = key(q);
           best = (q < n && kq < best) ? kq : best;
         }
         const int g = static_cast<int>(best & 0xFFFFu);
-        key_reg += (lane == g) ? 0x10000u : 0u;
+        // lane g's key becomes best with one more activated expert (a
+        // uniform value: one select); lane b records g
+        const uint32_t bumped = best + 0x10000u;
+        key_reg = (lane == g) ? bumped : key_reg;
         gsel = (lane == b) ? g : gsel;
       }
       if ((walked >> lane) & 1ull) assign[ch * kWave + lane] = gsel;
@@ -164,7 +178,11 @@ __device__ __forceinline__ uint64_t walker_gpus(const unsigned long long* adj, i
   uint64_t todo = ballot(a != 0ull);
   uint64_t mine = 0ull;
   for (int i = 0; todo != 0ull; ++i) {
-    uint64_t comp = 1ull << __builtin_ctzll(todo);
+    // start from the lowest remaining GPU's whole row (it lists the GPU
+    // itself), which already holds its neighbours
+    const int g0 = __builtin_ctzll(todo);
+    uint64_t comp = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(a >> 32), g0))) << 32) |
+                    static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(a), g0));
     for (;;) {
       const uint64_t grown = comp | ballot((a & comp) != 0ull);
       if (grown == comp) break;

@@ -747,7 +747,7 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_permute_scan_kernel(
 // is the number of bits set (a token chooses an expert at most once), and
 // the place of pair (t, e) inside e's segment is the number of bits of e's
 // mask below t, the stable rank. The places do not depend on the
-// assignment, so they are computed while the greedy walks. The walkers
+// assignment, so they are counted while the greedy walks. The walkers
 // (waves 0..3, one per component group of the GPU graph, with at most 64
 // GPUs; else wave 0) visit the multi-copy experts in order (greedy_walk, or
 // greedy_walk_packed for tables of at most 4 columns) while the other waves
@@ -760,12 +760,68 @@ constexpr int kMaskPairsPerThread = kSmallPairs / kPlanThreads;
 
 __host__ __device__ constexpr int round4(int n) { return (n + 3) & ~3; }
 
+// Bits set in the first W <= N words of an LDS row, the N reads issued
+// before any is used (words past W reread the last and count nothing).
+template <int N>
+__device__ __forceinline__ int popc_words(const unsigned long long* row, int W) {
+  unsigned long long w[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) w[q] = row[q < W ? q : W - 1];
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < N; ++q) c += q < W ? __popcll(w[q]) : 0;
+  return c;
+}
+
 __host__ __device__ constexpr int mask_plan_ints(int T, int E, int k, int R) {
   const int W = (T + 63) / 64, e8 = (E + 8) & ~7;
   return round4(2 * W * E) + 2 * round4(e8) + 2 * round4(E) + 3 * round4(R) +
          round4(R > kWave ? R : kWave) + round4((E + 3) / 4) + round4(E * kMaxRep / 2) +
          2 * round4((T * k + 1) / 2) +
          (R <= kWave ? round4(kPlanWaves * R) + round4(R + 1) + 2 * round4(E) + 2 * kWave : 0);
+}
+
+// The destination ranks of one token's k slots as a 64-bit set (ranks < 64):
+// the N slot reads issued together (slots past k reread slot k - 1), then
+// their ranks.
+template <int N>
+__device__ __forceinline__ unsigned long long token_rank_set(const unsigned short* row, int k,
+                                                             const int* s_rank) {
+  int ids[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) ids[j] = row[j < k ? j : k - 1];
+  unsigned long long rm = 0ull;
+#pragma unroll
+  for (int j = 0; j < N; ++j) rm |= 1ull << s_rank[ids[j]];
+  return rm;
+}
+
+// Exclusive prefix sums of in[0, n) into out[0, n) by one wave, lane l
+// taking the run l P .. l P + P - 1 (P <= N): the run's reads issued
+// together, its sum, a wave scan of the sums, then the run written out.
+// Returns the total (wave-uniform).
+template <int N>
+__device__ __forceinline__ int wave_excl_scan_runs(const int* in, int* out, int n, int P, int lane) {
+  const int base = lane * P;
+  int v[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const int i = base + q;
+    v[q] = in[i < n ? i : n - 1];
+    v[q] = (q < P && i < n) ? v[q] : 0;
+  }
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < N; ++q) sum += v[q];
+  const int incl = wave_incl_scan(sum, lane);
+  int run = incl - sum;
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const int i = base + q;
+    if (q < P && i < n) out[i] = run;
+    run += v[q];
+  }
+  return __builtin_amdgcn_readlane(incl, kWave - 1);
 }
 
 // The end of the bitmask plan for at most 64 ranks, after s_rank holds every
@@ -775,10 +831,11 @@ __host__ __device__ constexpr int mask_plan_ints(int T, int E, int k, int R) {
 //  - the experts in (rank, id) order: each expert's place among the experts
 //    of its rank from ballot matching on the rank bits (lower lanes) and
 //    per-wave counts (earlier waves), plus the experts of lower ranks;
-//  - one block scan of the counts in that order gives every expert's offset,
-//    and a rank's offset is the scan at its first place.
+//  - one scan of the counts in that order, by a single wave
+//    (wave_excl_scan_runs), gives every expert's offset, and a rank's offset
+//    is the scan at its first place.
 // s_wr [16][R], s_rbase [R + 1], s_ord [E], s_scan [E] are LDS scratch
-// (s_wr zeroed by the caller).
+// (s_wr zeroed by the caller); s_wave[0] carries the total.
 __device__ __forceinline__ void finish_few_ranks(
     int T, int E, int k, int R, const int* s_rank, const int* s_counts,
     const unsigned short* s_idx, int* s_ded, int* s_wr, int* s_rbase, int* s_ord, int* s_scan,
@@ -788,20 +845,22 @@ __device__ __forceinline__ void finish_few_ranks(
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   if (wave < (T + kWave - 1) / kWave) {  // uniform per wave
-    // the token's ids are read with loads issued together (slots past k
-    // reread slot k - 1), then their ranks
+    // the token's ids are read with loads issued together (in a bucket of
+    // 4, 8 or 16 slots; slots past k reread slot k - 1), then their ranks
     unsigned long long rm = 0ull;
     if (tid < T) {
-      int ids[kMaxK];
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) ids[j] = s_idx[tid * k + (j < k ? j : k - 1)];
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) rm |= 1ull << s_rank[ids[j]];
+      const unsigned short* row = s_idx + tid * k;
+      rm = k <= 4 ? token_rank_set<4>(row, k, s_rank)
+         : k <= 8 ? token_rank_set<8>(row, k, s_rank) : token_rank_set<kMaxK>(row, k, s_rank);
     }
+    // the wave's count for rank r lands in lane r (independent ballots,
+    // then one LDS add per rank)
+    int cnt = 0;
     for (int r = 0; r < R; ++r) {
       const int c = __popcll(ballot((rm >> r) & 1ull));
-      if (lane == 0 && c > 0) atomicAdd(&s_ded[r], c);
+      cnt = lane == r ? c : cnt;
     }
+    if (lane < R && cnt > 0) atomicAdd(&s_ded[lane], cnt);
   }
   const int r = tid < E ? s_rank[tid] : R;  // R: past every rank
   const int nbits = 32 - __builtin_clz(static_cast<unsigned>(R));
@@ -834,10 +893,17 @@ __device__ __forceinline__ void finish_few_ranks(
     rank_of[tid] = r;
   }
   __syncthreads();
-  int total = 0;
-  const int ex = block_excl_scan(tid < E ? s_ord[tid] : 0, s_wave, &total);
-  if (tid < E) s_scan[tid] = ex;
+  // one wave scans the counts in (rank, id) order, P = ceil(E / 64) per
+  // lane; lane 63's inclusive sum is the total
+  if (wave == 0) {
+    const int P = (E + kWave - 1) / kWave;
+    const int all = P <= 4 ? wave_excl_scan_runs<4>(s_ord, s_scan, E, P, lane)
+                  : P <= 8 ? wave_excl_scan_runs<8>(s_ord, s_scan, E, P, lane)
+                           : wave_excl_scan_runs<kMaxE / kWave>(s_ord, s_scan, E, P, lane);
+    if (lane == 0) s_wave[0] = all;
+  }
   __syncthreads();
+  const int total = s_wave[0];
   if (tid < E) {
     const int o = s_scan[place];
     expert_offsets[tid] = o;
@@ -929,17 +995,27 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
     }
   }
   __syncthreads();
+  // The place of pair i inside its expert's segment: the tokens before it in
+  // the expert's mask. Pairs first..n-1 in steps of `step`.
+  auto places = [&](int first, int step) {
+    for (int i = first; i < n; i += step) {
+      const int e = s_idx[i], t = i / k, wt = t >> 6;
+      const unsigned long long* m = mask + e * W;
+      int c = __popcll(m[wt] & ((1ull << (t & 63)) - 1ull));
+      for (int q = 0; q < wt; ++q) c += __popcll(m[q]);
+      s_rk[i] = static_cast<unsigned short>(c);
+    }
+  };
   // the demand vector: an expert's count is the number of bits of its mask
   // (a token selects an expert at most once); active experts' valid
   // candidates to LDS; single-copy experts (and every expert without a
   // table) are placed at once
   if (tid < E) {
-    unsigned long long mw[kMaskMaxT / 64];
-#pragma unroll
-    for (int q = 0; q < kMaskMaxT / 64; ++q) mw[q] = q < W ? mask[tid * W + q] : 0ull;  // uniform test
-    int c = 0;
-#pragma unroll
-    for (int q = 0; q < kMaskMaxT / 64; ++q) c += __popcll(mw[q]);
+    // the expert's W mask words, loaded together in the narrowest of 4, 8
+    // or 16 reads (W is uniform)
+    const unsigned long long* mrow = mask + tid * W;
+    const int c = W <= 4 ? popc_words<4>(mrow, W)
+                : W <= 8 ? popc_words<8>(mrow, W) : popc_words<kMaskMaxT / 64>(mrow, W);
     s_counts[tid] = c;
     counts[tid] = c;
     if (rep == nullptr) {
@@ -985,30 +1061,23 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
   }
   __syncthreads();
   // With at most 64 GPUs the walk is split over waves 0..3 (one per SIMD),
-  // each taking whole components of the GPU graph, and waves 4..15 find the
-  // pairs' places; else wave 0 walks and waves 1..15 find the places.
+  // each taking whole components of the GPU graph; else wave 0 walks. The
+  // other waves find the pairs' places meanwhile.
   const int walkers = (few && rep != nullptr) ? 4 : 1;
   if (wave < walkers) {
     if (rep != nullptr) {
-      if (few) {
+      if (packed) {
+        if (maxrep <= 2) greedy_walk_packed<2>(E, maxrep, id_order, word, act, s_assign, adj, R, wave, walkers);
+        else greedy_walk_packed<kPackedRep>(E, maxrep, id_order, word, act, s_assign, adj, R, wave, walkers);
+      } else if (few) {
         const uint64_t gpus = walker_gpus(adj, R, wave, walkers);
-        if (gpus != 0ull) {
-          if (packed) greedy_walk_packed(E, maxrep, id_order, word, act, s_assign, gpus);
-          else greedy_walk<true>(E, maxrep, id_order, ncand, cand, act, s_assign, gpus);
-        }
+        if (gpus != 0ull) greedy_walk<true>(E, maxrep, id_order, ncand, cand, act, s_assign, gpus);
       } else {
         greedy_walk<false>(E, maxrep, id_order, ncand, cand, act, s_assign);
       }
     }
   } else {
-    // place of each pair inside its expert: earlier tokens in the expert's mask
-    for (int i = tid - walkers * kWave; i < n; i += kPlanThreads - walkers * kWave) {
-      const int e = s_idx[i], t = i / k, wt = t >> 6;
-      const unsigned long long* m = mask + e * W;
-      int c = __popcll(m[wt] & ((1ull << (t & 63)) - 1ull));
-      for (int q = 0; q < wt; ++q) c += __popcll(m[q]);
-      s_rk[i] = static_cast<unsigned short>(c);
-    }
+    places(tid - walkers * kWave, kPlanThreads - walkers * kWave);
   }
   __syncthreads();
   if (tid < E) {  // an expert's rank: its assignment, else its first-listed copy (in rr[0])
