@@ -59,7 +59,17 @@ __device__ __forceinline__ void row_team(int tpt, int& row, int& lane, int& stri
 // With SS (single-send dispatch), pos is the token's single-send row per slot
 // and n_rows the buffer's row capacity; a row shared by several slots (the
 // same destination rank) is written once, by its first slot.
-template <int NT, int U, bool ONE, bool SERIAL = false, bool SS = false>
+//
+// With PREF (one-row blocks), lanes 0..k-1 of each wave load the token's k
+// send rows before the row loads and each slot's row is a readlane, so that
+// load's latency overlaps the row loads; without it the rows are scalar
+// loads issued once the row data has arrived. Measured on MI355X (cold
+// cache): PREF is 3% faster for rows of 129-256 chunks (H = 2048, k = 6:
+// 83.4 against 85.9 us) but 9% slower for 257-512 chunks (H = 4096, k = 2:
+// 75.5 against 69.2 us, and no LDS reservation from 0 to 64 KiB recovers
+// it): the stores then start sooner and more scattered write streams are
+// open at once. At H = 7168 it made no difference.
+template <int NT, int U, bool ONE, bool SERIAL = false, bool SS = false, bool PREF = false>
 __global__ __launch_bounds__(NT) void dispatch_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ send, int T,
     int k, int cpr, int tpt, int capacity = 0) {
@@ -70,6 +80,15 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(
   const int n_rows = SS ? capacity : T * k;
   const u32x4* xr = x + (size_t)t * cpr;
   const int32_t* pr = pos + (size_t)t * k;
+  static_assert(!PREF || ONE, "the row prefetch needs one row per block");
+  int my_r = 0;
+  if constexpr (PREF) {
+    if (__lane_id() < k) my_r = pr[__lane_id()];
+  }
+  auto slot_row = [&](int j) -> int {
+    if constexpr (PREF) return __builtin_amdgcn_readlane(my_r, j);
+    else return pr[j];
+  };
   // SS: bit j set when slot j is the first of the token to carry its row;
   // formed once, while the first row loads are in flight
   uint32_t first = 0;
@@ -84,15 +103,15 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(
     if constexpr (SS) {
       if (c0 == lt) {
         for (int j = 0; j < k; ++j) {
-          const int r = pr[j];
+          const int r = slot_row(j);
           bool dup = false;
-          for (int jj = 0; jj < j; ++jj) dup |= (pr[jj] == r);
+          for (int jj = 0; jj < j; ++jj) dup |= (slot_row(jj) == r);
           first |= dup ? 0u : (1u << j);
         }
       }
     }
     for (int j = 0; j < k; ++j) {
-      const int r = pr[j];
+      const int r = slot_row(j);
       if (static_cast<unsigned>(r) >= static_cast<unsigned>(n_rows)) continue;  // bad pos: skipped
       if constexpr (SS) {
         if (!((first >> j) & 1u)) continue;
@@ -107,7 +126,13 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(
   }
 }
 
-template <int ACT, bool ONE>
+// U > 1: up to U chunks per lane are loaded before the row's expert id (two
+// dependent loads: src, then idx) is looked up, so the id's latency overlaps
+// the row loads (H = 2048, k = 6: 125 against 139 us; H = 4096: 2% less).
+// U == 1 (rows of more than 512 chunks): the id first, then one chunk at a
+// time; batching the loads there measured 11% slower (H = 7168, k = 8:
+// 2.61 against 2.35 ms).
+template <int ACT, bool ONE, int U>
 __global__ __launch_bounds__(kRowThreads) void standin_kernel(
     const u32x4* send, const int32_t* __restrict__ src, const int32_t* __restrict__ idx, u32x4* y,
     int n, int E, int cpr, int tpt) {  // y may alias send: each chunk is read, then written, by one lane
@@ -115,17 +140,40 @@ __global__ __launch_bounds__(kRowThreads) void standin_kernel(
   declare_lds_reserve(cpr);
   row_team<kRowThreads, ONE>(tpt, r, lt, stride);
   if (r >= n) return;
-  const int sr = src[r];
-  const int e = static_cast<unsigned>(sr) < static_cast<unsigned>(n) ? idx[sr] : 0;
-  const float scale = 1.0f + static_cast<float>(e) / static_cast<float>(E);
   const u32x4* in = send + (size_t)r * cpr;
   u32x4* out = y + (size_t)r * cpr;
-  for (int c = lt; c < cpr; c += stride) {
+  auto expert_scale = [&]() {
+    const int sr = src[r];
+    const int e = static_cast<unsigned>(sr) < static_cast<unsigned>(n) ? idx[sr] : 0;
+    return 1.0f + static_cast<float>(e) / static_cast<float>(E);
+  };
+  auto convert = [&](u32x4 v, float scale, int c) {
     float f[8];
-    unpack8<ACT>(to_uint4(__builtin_nontemporal_load(in + c)), f);
+    unpack8<ACT>(to_uint4(v), f);
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = keep_f32(f[i] * scale);  // product rounded to fp32
     __builtin_nontemporal_store(to_vec(pack8<ACT>(f)), out + c);
+  };
+  if constexpr (U == 1) {
+    const float scale = expert_scale();
+    for (int c = lt; c < cpr; c += stride) convert(__builtin_nontemporal_load(in + c), scale, c);
+  } else {
+    float scale = 0.0f;
+    for (int c0 = lt; c0 < cpr; c0 += stride * U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * stride;
+        if (c < cpr) v[u] = __builtin_nontemporal_load(in + c);
+      }
+      if (c0 == lt) scale = expert_scale();
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * stride;
+        if (c >= cpr) break;
+        convert(v[u], scale, c);
+      }
+    }
   }
 }
 
@@ -241,9 +289,19 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
 // Receiver fan-out of single-send rows: each single-send row q (token t =
 // ss_token[q]) is read once and written to the expert rows pos[t*k + j] of
 // every slot j that it carries (ss_row[t*k + j] == q). One row per block, so
-// the token, its slots' rows and their destinations are uniform (scalar
-// loads). Rows at or beyond n_ss = ss_rank_offsets[R] exit at once.
-template <int NT, int U>
+// the token, its slots' rows and their destinations are uniform. Rows at or
+// beyond n_ss = ss_rank_offsets[R] exit at once.
+//
+// With PREF the row's first loads go out before its token and the token's
+// (ss_row, pos) entries are looked up (lanes 0..k-1 of each wave load one
+// slot's entries, which are then readlanes), so those dependent lookups
+// overlap the row loads; without it they are scalar loads, the token's
+// before the row loads and each slot's after the row data arrived. PREF
+// measured faster for rows of at most 256 chunks (H = 2048, k = 6: 1.3%) and
+// for launches too small for the occupancy cap (decode, 1344 rows: 4.4%),
+// slower for long rows in large launches (H = 4096, k = 2: 3.6%; H = 7168,
+// k = 8: 8.9%), where more scattered write streams are then open at once.
+template <int NT, int U, bool PREF>
 __global__ __launch_bounds__(NT) void fanout_kernel(
     const u32x4* __restrict__ send_ss, const int32_t* __restrict__ n_ss_ptr,
     const int32_t* __restrict__ ss_token, const int32_t* __restrict__ ss_row,
@@ -251,27 +309,63 @@ __global__ __launch_bounds__(NT) void fanout_kernel(
   declare_lds_reserve(cpr);
   const int q = blockIdx.x;
   if (q >= *n_ss_ptr) return;
-  const int t = ss_token[q];
-  if (static_cast<unsigned>(t) >= static_cast<unsigned>(T)) return;
   const int n_rows = T * k;
-  const int32_t* sr = ss_row + (size_t)t * k;
-  const int32_t* pr = pos + (size_t)t * k;
   const u32x4* in = send_ss + (size_t)q * cpr;
-  for (int c0 = threadIdx.x; c0 < cpr; c0 += NT * U) {
+  if constexpr (PREF) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * NT;
+      const int c = threadIdx.x + u * NT;
       if (c < cpr) v[u] = __builtin_nontemporal_load(in + c);
     }
-    for (int j = 0; j < k; ++j) {
-      const int r = pr[j];
-      if (sr[j] != q || static_cast<unsigned>(r) >= static_cast<unsigned>(n_rows)) continue;
-      u32x4* dst = send + (size_t)r * cpr;
+    const int t = ss_token[q];
+    if (static_cast<unsigned>(t) >= static_cast<unsigned>(T)) return;  // uniform over the block
+    int my_s = -1, my_p = 0;
+    if (__lane_id() < k) {
+      my_s = ss_row[(size_t)t * k + __lane_id()];
+      my_p = pos[(size_t)t * k + __lane_id()];
+    }
+    for (int c0 = threadIdx.x; c0 < cpr; c0 += NT * U) {
+      if (c0 != threadIdx.x) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * NT;
+          if (c < cpr) v[u] = __builtin_nontemporal_load(in + c);
+        }
+      }
+      for (int j = 0; j < k; ++j) {
+        const int r = __builtin_amdgcn_readlane(my_p, j);
+        if (__builtin_amdgcn_readlane(my_s, j) != q ||
+            static_cast<unsigned>(r) >= static_cast<unsigned>(n_rows)) continue;
+        u32x4* dst = send + (size_t)r * cpr;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * NT;
+          if (c < cpr) __builtin_nontemporal_store(v[u], dst + c);
+        }
+      }
+    }
+  } else {
+    const int t = ss_token[q];
+    if (static_cast<unsigned>(t) >= static_cast<unsigned>(T)) return;
+    const int32_t* sr = ss_row + (size_t)t * k;
+    const int32_t* pr = pos + (size_t)t * k;
+    for (int c0 = threadIdx.x; c0 < cpr; c0 += NT * U) {
+      u32x4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + u * NT;
-        if (c < cpr) __builtin_nontemporal_store(v[u], dst + c);
+        if (c < cpr) v[u] = __builtin_nontemporal_load(in + c);
+      }
+      for (int j = 0; j < k; ++j) {
+        const int r = pr[j];
+        if (sr[j] != q || static_cast<unsigned>(r) >= static_cast<unsigned>(n_rows)) continue;
+        u32x4* dst = send + (size_t)r * cpr;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * NT;
+          if (c < cpr) __builtin_nontemporal_store(v[u], dst + c);
+        }
       }
     }
   }
@@ -413,7 +507,7 @@ hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T,
     dispatch_kernel<kRowThreads, 1, false><<<(T + per_blk - 1) / per_blk, kRowThreads, res, s>>>(
         xv, pos, sv, T, k, cpr, tpt);
   } else if (cpr <= 256) {
-    dispatch_kernel<128, 2, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
+    dispatch_kernel<128, 2, true, false, false, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
   } else if (cpr <= 512) {
     dispatch_kernel<kRowThreads, 2, true><<<T, kRowThreads, res, s>>>(xv, pos, sv, T, k, cpr, 0);
   } else {
@@ -441,7 +535,7 @@ hipError_t launch_single_send_dispatch(const void* x, const int32_t* ss_row, voi
     dispatch_kernel<kRowThreads, 1, false, false, true><<<(T + per_blk - 1) / per_blk, kRowThreads, res, s>>>(
         xv, ss_row, sv, T, k, cpr, tpt, cap);
   } else if (cpr <= 256) {
-    dispatch_kernel<128, 2, true, false, true><<<T, 128, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
+    dispatch_kernel<128, 2, true, false, true, true><<<T, 128, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
   } else if (cpr <= 512) {
     dispatch_kernel<kRowThreads, 2, true, false, true><<<T, kRowThreads, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
   } else {
@@ -463,11 +557,14 @@ hipError_t launch_single_send_expand(const void* send_ss, const int32_t* ss_rank
   const int grid = ss_capacity < T * k ? ss_capacity : T * k;
   const size_t res = if_many_blocks(fanout_reserve(cpr), grid);
   if (cpr <= 256)
-    fanout_kernel<kRowThreads, 1><<<grid, kRowThreads, res, s>>>(in, n_ss, ss_token, ss_row, pos,
-                                                                out, T, k, cpr);
+    fanout_kernel<kRowThreads, 1, true><<<grid, kRowThreads, res, s>>>(in, n_ss, ss_token, ss_row,
+                                                                      pos, out, T, k, cpr);
+  else if (grid < kMinBlocksToCap)
+    fanout_kernel<kRowThreads, 2, true><<<grid, kRowThreads, res, s>>>(in, n_ss, ss_token, ss_row,
+                                                                      pos, out, T, k, cpr);
   else
-    fanout_kernel<kRowThreads, 2><<<grid, kRowThreads, res, s>>>(in, n_ss, ss_token, ss_row, pos,
-                                                                out, T, k, cpr);
+    fanout_kernel<kRowThreads, 2, false><<<grid, kRowThreads, res, s>>>(in, n_ss, ss_token, ss_row,
+                                                                       pos, out, T, k, cpr);
   return hipGetLastError();
 }
 
@@ -480,14 +577,19 @@ hipError_t launch_standin(const void* send, const int32_t* src, const int32_t* i
   u32x4* out = static_cast<u32x4*>(y);
   if (cpr >= kOneRowChunks) {
     const size_t res = if_many_blocks(standin_reserve(cpr), n);
-    if (act == 1) standin_kernel<1, true><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
-    else standin_kernel<2, true><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
+    if (cpr > 512) {
+      if (act == 1) standin_kernel<1, true, 1><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
+      else standin_kernel<2, true, 1><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
+    } else {
+      if (act == 1) standin_kernel<1, true, 4><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
+      else standin_kernel<2, true, 4><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
+    }
   } else {
     const int tpt = threads_per_row(cpr);
     const int per_blk = kRowThreads / tpt;
     const int grid = (n + per_blk - 1) / per_blk;
-    if (act == 1) standin_kernel<1, false><<<grid, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, tpt);
-    else standin_kernel<2, false><<<grid, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, tpt);
+    if (act == 1) standin_kernel<1, false, 4><<<grid, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, tpt);
+    else standin_kernel<2, false, 4><<<grid, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, tpt);
   }
   return hipGetLastError();
 }
