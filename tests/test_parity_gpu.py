@@ -131,6 +131,57 @@ def test_ties_signed_zeros_nan_inf(E, k, R):
     check_meta(b, ref, T, k)
 
 
+def tie_logits(T, E, seed):
+    rng = np.random.default_rng(seed)
+    l = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    l[rng.random((T, E)) < 0.2] = -0.0
+    l[rng.random((T, E)) < 0.05] = np.nan
+    l[rng.random((T, E)) < 0.02] = np.inf
+    l[rng.random((T, E)) < 0.02] = -np.inf
+    return l
+
+
+# ties at batch sizes with many route blocks (64-144 tokens each, the last
+# one partial): E just past 128, E = 256, 384 with k = 16, and E = 1000
+BIG_TIES = [(40000, 132, 3, 4), (65536, 256, 8, 8), (70000, 384, 16, 12), (36000, 1000, 1, 10)]
+
+
+@pytest.mark.parametrize("T,E,k,R", BIG_TIES, ids=[f"T{t}_E{e}_k{k}" for t, e, k, _ in BIG_TIES])
+def test_ties_signed_zeros_nan_inf_many_blocks(T, E, k, R):
+    l = tie_logits(T, E, 11 + E)
+    w = synth.Workload("ties_big", T, E, k, 64, R, synth.F16, "none", False)
+    x = synth.make_x(w, 0)
+    say(f"[case] ties T={T} E={E} k={k}")
+    ref = oracle.route_and_layout(T, E, k, R, l)
+    b = run_gpu(w, l, x, None)
+    check_meta(b, ref, T, k)
+
+
+def test_topk_independent_of_batch_blocking():
+    """A token's ids and gate-weight bits do not depend on the batch around
+    it: the first 700 tokens of a 65536-token batch (512 route blocks of
+    1024 threads) equal the same 700 tokens routed alone (small blocks)."""
+    T, E, k, R = 65536, 256, 8, 8
+    l = tie_logits(T, E, 5)
+    l[: T // 2] = np.random.default_rng(6).standard_normal((T // 2, E)).astype(np.float32)
+    say("[case] top-k of a large batch against the same tokens alone")
+    big = synth.Workload("big", T, E, k, 64, R, synth.F16, "none", False)
+    small = synth.Workload("small", 700, E, k, 64, R, synth.F16, "none", False)
+    out = []
+    for wl, ll in ((big, l), (small, l[:700].copy())):
+        p = B.make_problem(wl.T, wl.E, wl.k, wl.H, wl.R, wl.act_dtype)
+        lt = torch.from_numpy(ll).cuda()
+        idx = torch.empty(wl.T * k, dtype=torch.int32, device="cuda")
+        wt = torch.empty(wl.T * k, dtype=torch.float32, device="cuda")
+        counts = torch.empty(E, dtype=torch.int32, device="cuda")
+        ws = torch.empty(B.moe_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+        B.moe_route(p, lt, idx, wt, counts, ws)
+        torch.cuda.synchronize()
+        out.append((idx.cpu().numpy()[: 700 * k], wt.cpu().numpy()[: 700 * k].view(np.uint32)))
+    assert np.array_equal(out[0][0], out[1][0]), "idx"
+    assert np.array_equal(out[0][1], out[1][1]), "w bits"
+
+
 @pytest.mark.parametrize("order", ["constrained", "id"])
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_random_replica_tables(order, seed):
