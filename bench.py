@@ -424,14 +424,19 @@ def backward_leg(B, w, b, flush, steps, ev, np, torch, synth, seed):
             "combine_backward_bytes": cb_bytes, "dispatch_backward_bytes": db_bytes}
 
 
-def stats_leg(P, w, b, steps, ev, np, torch):
+def stats_leg(P, w, b, flush, steps, ev, np, torch):
     """Routing statistics of the batch (send-counts matrix, co-selection
     histogram, max/mean, Gini, Dirichlet alpha, locality), timed over
     `steps` calls; plus the share of the tokens' expert pairs held by the
-    most frequent 0.8% of pairs, read from the co-selection histogram."""
+    most frequent 0.8% of pairs, read from the co-selection histogram. A fill
+    of the flush buffer before each call keeps the GPU busy while the host
+    enqueues the call's three launches, so the bracket holds kernel time,
+    not launch latency (and the inputs come from HBM)."""
     st = P.allocate_stats(b)
     marks = []
     for i in range(steps + 2):
+        if flush is not None:
+            flush.fill_(12.0)
         a, c = ev(), ev()
         a.record()
         P.routing_stats(b, st)
@@ -454,11 +459,12 @@ def stats_leg(P, w, b, steps, ev, np, torch):
             "top_0.8pct_pairs_share": round(cover, 4)}
 
 
-def eplb_leg(P, B, synth, np, torch, dev, steps, ev, seed):
+def eplb_leg(P, B, synth, np, torch, dev, flush, steps, ev, seed):
     """The greedy replica assignment against token-balanced (EPLB-style)
     routing on the replicated decode workload (the one workload with
     replicas): maximum activated experts and maximum pairs per GPU under
-    each, and the time of the token-balanced split."""
+    each, and the time of the token-balanced split (its two launches
+    enqueued behind a fill of the flush buffer, as in stats_leg)."""
     w = synth.DECODE
     logits, x = synth.make_logits(w, seed), synth.make_x(w, seed)
     rep = synth.replica_table(w)
@@ -472,6 +478,8 @@ def eplb_leg(P, B, synth, np, torch, dev, steps, ev, seed):
     sp = P.allocate_split(b)
     marks = []
     for i in range(steps + 2):
+        if flush is not None:
+            flush.fill_(13.0)
         a, c = ev(), ev()
         a.record()
         P.token_balanced_split(b, sp)
@@ -806,9 +814,9 @@ def main():
         res["backward"] = backward_leg(B, w, b, flush, args.backward_steps, ev, np, torch, synth,
                                        args.seed)
     if args.stats_steps > 0:
-        res["routing_stats"] = stats_leg(P, w, b, args.stats_steps, ev, np, torch)
+        res["routing_stats"] = stats_leg(P, w, b, flush, args.stats_steps, ev, np, torch)
     if args.eplb_steps > 0:
-        res["eplb"] = eplb_leg(P, B, synth, np, torch, dev, args.eplb_steps, ev, args.seed)
+        res["eplb"] = eplb_leg(P, B, synth, np, torch, dev, flush, args.eplb_steps, ev, args.seed)
     if args.graph_steps > 0:
         res["decode_graph"] = graph_leg(P, B, synth, np, torch, dev, args.graph_steps, args.seed)
     if cpu is not None:
