@@ -1,7 +1,7 @@
 """Out-of-range send positions and sources reach only the kernels' own bounds
 checks: each row kernel tests every pos and src entry against the buffer it
-addresses, so a corrupt entry is skipped rather than followed. Dispatch
-leaves the row the slot would have written untouched; combine and dispatch
+addresses, so a corrupt entry is skipped rather than followed. Dispatch and
+the single-send fan-out leave the row the slot would have written untouched; combine and dispatch
 backward add nothing for it; combine backward writes no dy row and a dw of
 0; the stand-in scales a row whose source is out of range as expert 0. Every
 other output equals the oracle's on the same corrupted tables (the oracle
@@ -41,7 +41,9 @@ def with_zero_row(rows: np.ndarray) -> np.ndarray:
 
 SHAPES = [
     ("H264_k6", 600, 64, 6, 264, 8),     # several rows per block, combine one chunk position per step
-    ("H2056_k2", 400, 16, 2, 2056, 4),   # 128-thread blocks, two chunks per lane
+    ("H1040_k5", 300, 32, 5, 1040, 8),   # 130 chunks: one-row blocks with the slots' rows loaded by lanes
+    ("H2048_k3", 350, 16, 3, 2048, 4),   # 256 chunks: the same, at the widest such row
+    ("H2056_k2", 400, 16, 2, 2056, 4),   # 257 chunks: 256-thread blocks, two chunks per lane
     ("H4104_k4", 300, 32, 4, 4104, 8),   # rows past 512 chunks
 ]
 
@@ -73,6 +75,20 @@ def test_out_of_range_positions_are_skipped(name, T, E, k, H, R):
     assert (got[orphan] == SENTINEL).all(), "dispatch wrote a row no valid slot targets"
     keep = np.flatnonzero(~orphan)
     assert np.array_equal(got[keep], oracle.dispatch_rows(x, ref["src"], k, keep)), "dispatch rows"
+
+    # receiver fan-out of valid single-send rows with the corrupted pos: a
+    # slot whose destination is out of range writes nothing
+    ss = P.allocate_single_send(b)
+    P.layout_single_send(b, ss)
+    P.single_send_dispatch(b, ss)
+    expanded = torch.empty_like(b.send)
+    expanded.view(torch.int16).fill_(SENTINEL)
+    B.moe_single_send_expand(p, ss.send_ss, ss.ss_rank_offsets, ss.ss_token, ss.ss_row, pos_t,
+                             expanded)
+    torch.cuda.synchronize()
+    got_x = tensor_bits(expanded)
+    assert (got_x[orphan] == SENTINEL).all(), "fan-out wrote a row no valid slot targets"
+    assert np.array_equal(got_x[keep], oracle.dispatch_rows(x, ref["src"], k, keep)), "fan-out rows"
 
     # combine over the GPU's y (checked elsewhere): a skipped slot adds nothing
     y_bits = tensor_bits(b.y)
