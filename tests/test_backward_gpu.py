@@ -172,10 +172,12 @@ def test_backward_edge_shapes(name, T, E, k, R, H):
     run_backward(synth.Workload(name, T, E, k, H, R, synth.BF16, "none", False), 5)
 
 
-# Row widths past the one-chunk shape (16-byte chunks per row: 257, 375,
-# 513, 1024, 1537), k up to 8 (two chunk positions per step).
-WIDTHS = [("H2056_k3", 2056, 3), ("H3000_k8", 3000, 8), ("H4104_k4", 4104, 4),
-          ("H8192_k6", 8192, 6), ("H12296_k7", 12296, 7)]
+# Row widths (16-byte chunks per row: 129 and 256, the one-row blocks with
+# one chunk position per step and the pos entries loaded by lanes; then 257,
+# 375, 513, 1024, 1537, two chunk positions per step), k up to 8.
+WIDTHS = [("H1032_k5", 1032, 5), ("H2048_k2", 2048, 2), ("H2056_k3", 2056, 3),
+          ("H3000_k8", 3000, 8), ("H4104_k4", 4104, 4), ("H8192_k6", 8192, 6),
+          ("H12296_k7", 12296, 7)]
 
 
 @pytest.mark.parametrize("name,H,k", WIDTHS, ids=[v[0] for v in WIDTHS])

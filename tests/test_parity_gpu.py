@@ -94,7 +94,8 @@ EDGE = [
 # 513, 768 and 1024 (the 128-thread dispatch with 5, 6 and 8 chunks per
 # lane), 1537 (rows past 1024 chunks: the dispatch loops); k from 3 to 8
 # covers the combine's compile-time-k instances.
-WIDTHS = [("H2056_k3", 2056, 3), ("H3000_k5", 3000, 5), ("H4104_k4", 4104, 4),
+WIDTHS = [("H1024_k4", 1024, 4), ("H1032_k2", 1032, 2), ("H2048_k6", 2048, 6),
+          ("H2056_k3", 2056, 3), ("H3000_k5", 3000, 5), ("H4104_k4", 4104, 4),
           ("H6144_k6", 6144, 6), ("H8192_k8", 8192, 8), ("H12296_k7", 12296, 7)]
 
 

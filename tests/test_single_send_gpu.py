@@ -124,10 +124,12 @@ def test_single_send_edge_shapes(name, T, E, k, R, H):
     check_single_send(w, b, ss, ex, ref)
 
 
-# Row widths (16-byte chunks per row: 257, 375, 513, 1024, 1537): the
-# dispatch's long-row shapes and the fan-out's two chunks per lane.
-WIDTHS = [("H2056_k3", 2056, 3), ("H3000_k5", 3000, 5), ("H4104_k4", 4104, 4),
-          ("H8192_k8", 8192, 8), ("H12296_k7", 12296, 7)]
+# Row widths (16-byte chunks per row: 129 and 256, the shapes whose
+# dispatch and fan-out load the slots' rows by lanes; 257, 375, 513, 1024,
+# 1537: the dispatch's long-row shapes and the fan-out's two chunks per lane).
+WIDTHS = [("H1032_k3", 1032, 3), ("H2048_k6", 2048, 6), ("H2056_k3", 2056, 3),
+          ("H3000_k5", 3000, 5), ("H4104_k4", 4104, 4), ("H8192_k8", 8192, 8),
+          ("H12296_k7", 12296, 7)]
 
 
 @pytest.mark.parametrize("name,H,k", WIDTHS, ids=[v[0] for v in WIDTHS])
