@@ -488,8 +488,7 @@ hipError_t launch_combine_a(const u32x4* y, const int32_t* pos, const float* w, 
 //  - 129-256 chunks: 128-thread blocks, two chunks per lane, one row per
 //    block. Against 256-thread blocks with one chunk per lane (48 KiB):
 //    H = 2048, k = 2: 70 vs 90 us; H = 1536, k = 2: 56 vs 85 us; H = 1280,
-//    k = 4: 77 vs 98 us; H = 2048, k = 6: 86 us either way; the slots'
-//    send rows loaded by lanes beside the row loads (PREF);
+//    k = 4: 77 vs 98 us; H = 2048, k = 6: 86 us either way;
 //  - 257-512 chunks: 256-thread blocks, two chunks per lane;
 //  - longer rows (H = 7168): 128-thread blocks with ceil(cpr / 128) chunks
 //    per lane and serialized row loads (1.63 ms against 1.69-1.77 ms for
