@@ -12,7 +12,9 @@ from .binding import (MOE_BF16, MOE_F16, MOE_FLAG_GREEDY_ID_ORDER, MOE_FLAG_OUT_
                       MoeError, Problem, make_problem, moe_assign_replicas, moe_combine,
                       moe_combine_backward, moe_dispatch_backward,
                       moe_dispatch, moe_expert_standin, moe_last_error, moe_layout,
-                      moe_layout_single_send, moe_route, moe_routing_stats, moe_single_send_dispatch,
+                      moe_layout_single_send, moe_route, moe_route_assign_layout,
+                      moe_route_assign_layout_noalloc, moe_route_assign_layout_single_send,
+                      moe_routing_stats, moe_single_send_dispatch,
                       moe_single_send_expand, moe_status_string, moe_token_balanced_split,
                       moe_version,
                       moe_workspace_bytes)

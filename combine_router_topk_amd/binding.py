@@ -31,7 +31,8 @@ MOE_NOALLOC_SCRATCH_BYTES = 2 << 20
 
 EXPORTED = ("moe_version", "moe_build_id", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
             "moe_route", "moe_assign_replicas", "moe_layout", "moe_route_assign_layout",
-            "moe_route_assign_layout_noalloc", "moe_layout_single_send",
+            "moe_route_assign_layout_noalloc", "moe_route_assign_layout_single_send",
+            "moe_layout_single_send",
             "moe_single_send_dispatch", "moe_single_send_expand", "moe_dispatch",
             "moe_expert_standin", "moe_combine", "moe_combine_backward", "moe_dispatch_backward",
             "moe_routing_stats", "moe_token_balanced_split")
@@ -74,6 +75,8 @@ def _load() -> ctypes.CDLL:
                                           vp, vp, sz, vp]),
         "moe_route_assign_layout_noalloc": (i32, [P, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                                   vp, vp, vp, vp]),
+        "moe_route_assign_layout_single_send": (i32, [P, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
+                                                      vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_layout_single_send": (i32, [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, sz, vp]),
         "moe_single_send_dispatch": (i32, [P, vp, vp, vp, i32, vp]),
@@ -215,6 +218,27 @@ def moe_route_assign_layout(p: Problem, logits, rep, maxrep: int, idx, w, counts
         _ptr(pos, torch.int32, n, "pos"), _ptr(src, torch.int32, n, "src"),
         _ptr(dedup, torch.int32, p.R, "dedup"), _ptr(ws, None, None, "ws"), _nbytes(ws),
         _stream(stream)), "moe_route_assign_layout")
+
+
+def moe_route_assign_layout_single_send(p: Problem, logits, rep, maxrep: int, idx, w, counts,
+                                        assign, active, rank_of, expert_offsets, rank_offsets,
+                                        pos, src, dedup, ss_rank_offsets, ss_row, ss_token, ws,
+                                        stream=None) -> None:
+    n = p.T * p.k
+    _check(_lib.moe_route_assign_layout_single_send(
+        ctypes.byref(p), _ptr(logits, torch.float32, p.T * p.E, "logits"),
+        _ptr(rep, torch.int32, p.E * maxrep if rep is not None else 0, "rep"), maxrep,
+        _ptr(idx, torch.int32, n, "idx"), _ptr(w, torch.float32, n, "w"),
+        _ptr(counts, torch.int32, p.E, "counts"), _ptr(assign, torch.int32, p.E, "assign"),
+        _ptr(active, torch.int32, p.R, "active"), _ptr(rank_of, torch.int32, p.E, "rank_of"),
+        _ptr(expert_offsets, torch.int32, p.E, "expert_offsets"),
+        _ptr(rank_offsets, torch.int32, p.R + 1, "rank_offsets"),
+        _ptr(pos, torch.int32, n, "pos"), _ptr(src, torch.int32, n, "src"),
+        _ptr(dedup, torch.int32, p.R, "dedup"),
+        _ptr(ss_rank_offsets, torch.int32, p.R + 1, "ss_rank_offsets"),
+        _ptr(ss_row, torch.int32, n, "ss_row"), _ptr(ss_token, torch.int32, n, "ss_token"),
+        _ptr(ws, None, None, "ws"), _nbytes(ws), _stream(stream)),
+        "moe_route_assign_layout_single_send")
 
 
 def moe_route_assign_layout_noalloc(p: Problem, logits, rep, maxrep: int, idx, w, counts, assign,

@@ -142,7 +142,7 @@ moe_status check_route_assign_layout(const moe_problem* p, const float* logits, 
 
 extern "C" {
 
-int32_t moe_version(void) { return 1 * 10000 + 1 * 100 + 0; }
+int32_t moe_version(void) { return 1 * 10000 + 2 * 100 + 0; }
 
 const char* moe_build_id(void) { return MOE_BUILD_ID; }
 
@@ -218,6 +218,33 @@ moe_status moe_route_assign_layout(const moe_problem* p, const float* logits, co
                         (p->flags & MOE_FLAG_GREEDY_ID_ORDER) != 0, idx, w, counts, assign, active,
                         rank_of, expert_offsets, rank_offsets, pos, src, dedup,
                         static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+moe_status moe_route_assign_layout_single_send(
+    const moe_problem* p, const float* logits, const int32_t* rep, int32_t maxrep, int32_t* idx,
+    float* w, int32_t* counts, int32_t* assign, int32_t* active, int32_t* rank_of,
+    int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos, int32_t* src, int32_t* dedup,
+    int32_t* ss_rank_offsets, int32_t* ss_row, int32_t* ss_token, void* ws, size_t ws_bytes,
+    void* stream) {
+  const char* fn = "moe_route_assign_layout_single_send";
+  CHECK(check_route_assign_layout(p, logits, rep, maxrep, idx, w, counts, assign, active, rank_of,
+                                  expert_offsets, rank_offsets, pos, src, dedup, fn));
+  CHECK(need(ss_rank_offsets, 4, fn, "ss_rank_offsets"));
+  if (p->T > 0) {
+    CHECK(need(ss_row, 4, fn, "ss_row"));
+    CHECK(need(ss_token, 4, fn, "ss_token"));
+  }
+  CHECK(need(ws, 256, fn, "ws"));
+  const size_t req = moe::workspace_bytes(p->T, p->E, p->R);
+  if (ws_bytes < req) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, req);
+  clear_stale_error();
+  return hip_status(moe::launch_route_assign_layout_single_send(
+                        logits, p->T, p->E, p->k, p->R, rep, maxrep,
+                        (p->flags & MOE_FLAG_GREEDY_ID_ORDER) != 0, idx, w, counts, assign, active,
+                        rank_of, expert_offsets, rank_offsets, pos, src, dedup, ss_rank_offsets,
+                        ss_row, ss_token, static_cast<int32_t*>(ws),
+                        static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -46,9 +46,12 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
 // null), no counts.
 // With ded_rows (and ws; R | E, contiguous partition), also one row per route block
 // of per-rank token counts ([route_nblk, R]: tokens of the block with at
-// least one selected expert on the rank).
+// least one selected expert on the rank), and with lead as well each token's
+// leader mask ([T]: bit j set when slot j is the token's first slot on its
+// rank).
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
-                             int32_t* ws, hipStream_t s, int32_t* ded_rows = nullptr, int R = 1);
+                             int32_t* ws, hipStream_t s, int32_t* ded_rows = nullptr, int R = 1,
+                             int32_t* lead = nullptr);
 
 // route, assign and layout of one batch: for a small batch the top-k kernel
 // and one workgroup that does everything else, else the three launches.
@@ -58,6 +61,16 @@ hipError_t launch_route_assign_layout(const float* logits, int T, int E, int k, 
                                       int32_t* rank_of, int32_t* expert_offsets,
                                       int32_t* rank_offsets, int32_t* pos, int32_t* src,
                                       int32_t* dedup, int32_t* ws, hipStream_t s);
+
+// route, assign and layout with the single-send rows: for a batch without a
+// replica table the top-k kernel (with leader masks), the column scan and
+// one permutation + single-send launch; else the separate calls' kernels.
+// ws as for launch_route_assign_layout plus T ints.
+hipError_t launch_route_assign_layout_single_send(
+    const float* logits, int T, int E, int k, int R, const int32_t* rep, int maxrep, bool id_order,
+    int32_t* idx, float* w, int32_t* counts, int32_t* assign, int32_t* active, int32_t* rank_of,
+    int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos, int32_t* src, int32_t* dedup,
+    int32_t* ss_rank_offsets, int32_t* ss_row, int32_t* ss_token, int32_t* ws, hipStream_t s);
 
 hipError_t launch_assign(const int32_t* counts, int E, int R, const int32_t* rep, int maxrep,
                          bool id_order, int32_t* assign, int32_t* active, hipStream_t s);

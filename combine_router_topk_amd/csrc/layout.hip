@@ -616,15 +616,17 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_small_kernel(
 // One workgroup per task of 64 columns: the expert tasks replace their
 // columns of the histogram rows with exclusive prefixes over blocks (the
 // block's first row per expert) and write the totals as counts, with
-// rank_of and assign; the rank tasks sum their columns into dedup. The 16
+// rank_of and assign; the rank tasks sum their columns into dedup (and with
+// ded_prefix replace them with their exclusive prefixes as well: the
+// block's first single-send row per rank). The 16
 // waves split the rows (at most kSumRows each, so 512 route blocks) and load
 // their segment at once.
 constexpr int kSumRows = 32;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_scan_kernel(
-    int32_t* __restrict__ hist, const int32_t* __restrict__ ded, int nblk, int E, int R, int per,
+    int32_t* __restrict__ hist, int32_t* __restrict__ ded, int nblk, int E, int R, int per,
     int32_t* __restrict__ counts, int32_t* __restrict__ assign, int32_t* __restrict__ rank_of,
-    int32_t* __restrict__ dedup) {
+    int32_t* __restrict__ dedup, int ded_prefix) {
   __shared__ int part[kPlanWaves][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -666,8 +668,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scan_kernel(
       rank_of[c] = c / per;
       assign[c] = all > 0 ? c / per : -1;
     }
-  } else if (wave == 0) {
-    dedup[c] = all;
+  } else {
+    if (ded_prefix) {  // uniform: a kernel argument
+      int run = pre;
+#pragma unroll
+      for (int i = 0; i < kSumRows; ++i) {
+        const int r = r_lo + i;
+        if (r < r_hi) ded[(size_t)r * R + c] = run;
+        run += v[i];
+      }
+    }
+    if (wave == 0) dedup[c] = all;
   }
 }
 
@@ -738,6 +749,130 @@ __global__ __launch_bounds__(WAVES * kWave) void layout_permute_scan_kernel(
   const int64_t i0 = (int64_t)b * tpb * k;
   const int64_t i1 = min((int64_t)T * k, i0 + (int64_t)tpb * k);
   permute_rounds<WAVES>(idx, i0, i1, E, T * k, run, wcnt, wtag, pos, src);
+}
+
+// The permutation and the single-send rows of one route block for a batch
+// without a replica table, after plan_scan_kernel with ded_prefix (ss_base:
+// the block's first single-send row per rank, relative to the rank's
+// start). Prologue: the expert scan of layout_permute_scan_kernel (block 0
+// writing expert_offsets, rank_offsets and active) and, beside it, the
+// exclusive scan of dedup over ranks (block 0 writing ss_rank_offsets); the
+// block's single-send cursors stay in registers through the permutation
+// rounds. Then the single-send rounds of layout_permute_ss_kernel, reusing
+// the permutation's LDS tables, with rank e / per for expert e.
+// LDS: max((1 + 2 WAVES) E + R, E + (1 + 2 WAVES) R) ints.
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void layout_permute_ss_scan_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int R, int per, int tpb,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ ss_base, const int32_t* __restrict__ dedup,
+    const int32_t* __restrict__ lead_mask, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ active, int32_t* __restrict__ pos,
+    int32_t* __restrict__ src, int32_t* __restrict__ ss_rank_offsets, int32_t* __restrict__ ss_row,
+    int32_t* __restrict__ ss_token) {
+  constexpr int kThreads = WAVES * kWave;
+  constexpr int kRun = (kMaxE + kThreads - 1) / kThreads;
+  constexpr int kRunR = (kMaxR + kThreads - 1) / kThreads;
+  extern __shared__ int smem[];
+  __shared__ int s_wsum[WAVES];
+  __shared__ int s_wsum_r[WAVES];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  // every load first: counts and this block's expert prefixes, dedup and
+  // this block's single-send prefixes, each thread a run of consecutive ids
+  const int n_run = (E + kThreads - 1) / kThreads;
+  const int e0 = threadIdx.x * n_run;
+  const int n_run_r = (R + kThreads - 1) / kThreads;
+  const int q0 = threadIdx.x * n_run_r;
+  int c[kRun], bs[kRun], cr[kRunR], sb[kRunR];
+  int sum = 0, sum_r = 0;
+#pragma unroll
+  for (int i = 0; i < kRun; ++i) {
+    const int e = e0 + i;
+    const bool ok = i < n_run && e < E;
+    c[i] = ok ? counts[e] : 0;
+    bs[i] = ok ? base[(size_t)b * E + e] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kRunR; ++i) {
+    const int r = q0 + i;
+    const bool ok = i < n_run_r && r < R;
+    cr[i] = ok ? dedup[r] : 0;
+    sb[i] = ok ? ss_base[(size_t)b * R + r] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kRun; ++i) sum += c[i];
+#pragma unroll
+  for (int i = 0; i < kRunR; ++i) sum_r += cr[i];
+  int* run = smem;                   // [E] next free row of each expert
+  int* wcnt = smem + E;              // [WAVES][E]
+  int* wtag = smem + E + WAVES * E;  // [WAVES][E]
+  int* s_act = wtag + WAVES * E;     // [R] (block 0)
+  for (int i = threadIdx.x; i < WAVES * E; i += kThreads) wtag[i] = 0;
+  if (b == 0)
+    for (int r = threadIdx.x; r < R; r += kThreads) s_act[r] = 0;
+  const int incl = wave_incl_scan(sum, lane);
+  const int incl_r = wave_incl_scan(sum_r, lane);
+  if (lane == kWave - 1) {
+    s_wsum[wave] = incl;
+    s_wsum_r[wave] = incl_r;
+  }
+  __syncthreads();
+  int off = incl - sum, off_r = incl_r - sum_r, n_ss = 0;
+#pragma unroll
+  for (int i = 0; i < WAVES; ++i) {
+    off += (i < wave) ? s_wsum[i] : 0;
+    off_r += (i < wave) ? s_wsum_r[i] : 0;
+    n_ss += s_wsum_r[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kRun; ++i) {
+    const int e = e0 + i;
+    if (i < n_run && e < E) {
+      run[e] = off + bs[i];
+      if (b == 0) {
+        expert_offsets[e] = off;
+        if (e % per == 0) rank_offsets[e / per] = off;
+        if (c[i] > 0) atomicAdd(&s_act[e / per], 1);
+      }
+      off += c[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRunR; ++i) {  // the block's single-send cursors, kept in sb
+    const int r = q0 + i;
+    if (i < n_run_r && r < R) {
+      if (b == 0) ss_rank_offsets[r] = off_r;
+      sb[i] += off_r;
+      off_r += cr[i];
+    }
+  }
+  __syncthreads();
+  if (b == 0) {
+    for (int r = threadIdx.x; r < R; r += kThreads) active[r] = s_act[r];
+    if (threadIdx.x == 0) {
+      rank_offsets[R] = T * k;
+      ss_rank_offsets[R] = n_ss;
+    }
+  }
+  const int64_t i0 = (int64_t)b * tpb * k;
+  const int64_t i1 = min((int64_t)T * k, i0 + (int64_t)tpb * k);
+  permute_rounds<WAVES>(idx, i0, i1, E, T * k, run, wcnt, wtag, pos, src);  // ends with a barrier
+  int* s_rank = smem;                    // [E]
+  int* run_r = smem + E;                 // [R] next free single-send row of each rank
+  int* wcnt_r = smem + E + R;            // [WAVES][R]
+  int* wtag_r = smem + E + R + WAVES * R;  // [WAVES][R]
+  for (int e = threadIdx.x; e < E; e += kThreads) s_rank[e] = e / per;
+  for (int i = threadIdx.x; i < WAVES * R; i += kThreads) wtag_r[i] = 0;
+#pragma unroll
+  for (int i = 0; i < kRunR; ++i) {
+    const int r = q0 + i;
+    if (i < n_run_r && r < R) run_r[r] = sb[i];
+  }
+  __syncthreads();
+  single_send_rounds<WAVES>(idx, i0, i1, k, E, R, T * k, s_rank, run_r, wcnt_r, wtag_r, lead_mask,
+                            ss_row, ss_token);
 }
 
 // The routing plan of a decode-sized batch (T <= 1024 tokens, T k <= 8192
@@ -1214,7 +1349,7 @@ hipError_t launch_route_assign_layout(const float* logits, int T, int E, int k, 
     if (err != hipSuccess) return err;
     const int tasks = (E + kWave - 1) / kWave + (R + kWave - 1) / kWave;
     plan_scan_kernel<<<tasks, kPlanThreads, 0, s>>>(hist, ded, nblk, E, R, per, counts, assign,
-                                                    rank_of, dedup);
+                                                    rank_of, dedup, 0);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (E <= 256 && (int64_t)bl.route_tpb * k >= 1024)
@@ -1233,6 +1368,49 @@ hipError_t launch_route_assign_layout(const float* logits, int T, int E, int k, 
   if (err != hipSuccess) return err;
   return launch_layout(idx, T, E, k, R, assign, rep, rep ? maxrep : 1, rank_of, expert_offsets,
                        rank_offsets, pos, src, dedup, nullptr, nullptr, nullptr, ws, s);
+}
+
+hipError_t launch_route_assign_layout_single_send(
+    const float* logits, int T, int E, int k, int R, const int32_t* rep, int maxrep, bool id_order,
+    int32_t* idx, float* w, int32_t* counts, int32_t* assign, int32_t* active, int32_t* rank_of,
+    int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos, int32_t* src, int32_t* dedup,
+    int32_t* ss_rank_offsets, int32_t* ss_row, int32_t* ss_token, int32_t* ws, hipStream_t s) {
+  if (rep == nullptr && T > 0) {
+    // no replica table: top-k with per-block counts and leader masks, the
+    // column scan (expert and rank columns to prefixes), then the
+    // permutation and the single-send rows
+    const Blocking bl = blocking_for(T, E, R);
+    const int nblk = bl.route_nblk, per = E / R;
+    int32_t* hist = ws;                          // [nblk, E]
+    int32_t* ded = ws + (size_t)nblk * E;        // [nblk, R]
+    int32_t* lead = ded + (size_t)nblk * R;      // [T]
+    hipError_t err = launch_route_topk(logits, T, E, k, idx, w, hist, s, ded, R, lead);
+    if (err != hipSuccess) return err;
+    const int tasks = (E + kWave - 1) / kWave + (R + kWave - 1) / kWave;
+    plan_scan_kernel<<<tasks, kPlanThreads, 0, s>>>(hist, ded, nblk, E, R, per, counts, assign,
+                                                    rank_of, dedup, 1);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const bool w16 = (int64_t)bl.route_tpb * k >= 1024 && E <= 256 && E + 33 * R <= 12 * 1024;
+    const int W = w16 ? 16 : 4;
+    const size_t pe = (size_t)(1 + 2 * W) * E + R, pr = (size_t)E + (size_t)(1 + 2 * W) * R;
+    const size_t lds = (pe > pr ? pe : pr) * sizeof(int);
+    if (w16)
+      layout_permute_ss_scan_kernel<16><<<nblk, 16 * kWave, lds, s>>>(
+          idx, T, E, k, R, per, bl.route_tpb, hist, counts, ded, dedup, lead, expert_offsets,
+          rank_offsets, active, pos, src, ss_rank_offsets, ss_row, ss_token);
+    else
+      layout_permute_ss_scan_kernel<4><<<nblk, 4 * kWave, lds, s>>>(
+          idx, T, E, k, R, per, bl.route_tpb, hist, counts, ded, dedup, lead, expert_offsets,
+          rank_offsets, active, pos, src, ss_rank_offsets, ss_row, ss_token);
+    return hipGetLastError();
+  }
+  hipError_t err = launch_route(logits, T, E, k, idx, w, counts, ws, s);
+  if (err != hipSuccess) return err;
+  err = launch_assign(counts, E, R, rep, rep ? maxrep : 1, id_order, assign, active, s);
+  if (err != hipSuccess) return err;
+  return launch_layout(idx, T, E, k, R, assign, rep, rep ? maxrep : 1, rank_of, expert_offsets,
+                       rank_offsets, pos, src, dedup, ss_rank_offsets, ss_row, ss_token, ws, s);
 }
 
 }  // namespace moe

@@ -34,12 +34,14 @@ constexpr int kRouteTargetBlocks = 512;
 // With ded_rows set (contiguous partition, per = E / R experts per rank),
 // each block also counts, per rank, its tokens with at least one selected
 // expert on that rank (the single-send counts), written as one row of a
-// [blocks, R] matrix beside the expert histogram.
+// [blocks, R] matrix beside the expert histogram; with lead set as well,
+// lead[t] is token t's leader mask (bit j: slot j is the token's first slot
+// on its rank).
 template <int L, int V, int NT>
 __global__ __launch_bounds__(NT) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int tpb, int32_t* __restrict__ idx,
     float* __restrict__ w, int32_t* __restrict__ block_hist, int32_t* __restrict__ ded_rows, int R,
-    int per) {
+    int per, int32_t* __restrict__ lead) {
   extern __shared__ int s_hist[];
   int* s_ded = s_hist + E;  // [R], used with ded_rows
   constexpr int TPW = kWave / L;  // tokens per wave step
@@ -134,6 +136,11 @@ __global__ __launch_bounds__(NT) void route_topk_kernel(
         dup |= (jj < sl) && (o == rk);
       }
       if (valid && sl < k && !dup) atomicAdd(&s_ded[rk], 1);
+      if (lead != nullptr) {  // uniform: a kernel argument
+        // bit j: slot j is the token's first slot on its rank
+        const uint64_t lm = (ballot(valid && sl < k && !dup) & gmask) >> (grp * L);
+        if (valid && sl == 0) lead[t] = static_cast<int32_t>(lm);
+      }
     }
   }
   __syncthreads();
@@ -159,12 +166,12 @@ __global__ __launch_bounds__(NT) void route_topk_kernel(
 // rounded up to a power of two): token s of a batch keeps its slot j in lane
 // s KP + j, and one fp64 pass evaluates the whole batch. Evaluated per token,
 // the softmax used k of the 64 lanes for the cost of all.
-// ded_rows, R and per as in route_topk_kernel.
+// ded_rows, R, per and lead as in route_topk_kernel.
 template <int V, int KP, int NT>
 __global__ __launch_bounds__(NT) void route_topk_wave_kernel(
     const float* __restrict__ logits, int T, int E, int k, int tpb, int32_t* __restrict__ idx,
     float* __restrict__ w, int32_t* __restrict__ block_hist, int32_t* __restrict__ ded_rows, int R,
-    int per) {
+    int per, int32_t* __restrict__ lead) {
   extern __shared__ int s_hist[];
   int* s_ded = s_hist + E;  // [R], used with ded_rows
   const int lane = threadIdx.x & (kWave - 1);
@@ -219,6 +226,11 @@ __global__ __launch_bounds__(NT) void route_topk_wave_kernel(
         dup |= (jj < j) && (o == rk);
       }
       if (on && !dup) atomicAdd(&s_ded[rk], 1);
+      if (lead != nullptr) {  // uniform: a kernel argument
+        // bit j: slot j is the token's first slot on its rank
+        const uint64_t lm = ballot(on && !dup) >> (lane & ~(KP - 1));
+        if (on && j == 0) lead[b_t] = static_cast<int32_t>(lm & ((KP < 64 ? (1ull << KP) : 0ull) - 1ull));
+      }
     }
   };
 
@@ -316,6 +328,7 @@ struct TopkArgs {
   int32_t* hist;
   int32_t* ded;  // null: no per-rank counts
   int R, per;
+  int32_t* lead;  // null: no leader masks (needs ded)
   size_t lds() const { return (size_t)(E + (ded != nullptr ? R : 0)) * sizeof(int); }
 };
 
@@ -323,10 +336,10 @@ template <int L, int V>
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.threads == kRouteThreadsSmall)
     route_topk_kernel<L, V, kRouteThreadsSmall><<<a.nblk, kRouteThreadsSmall, a.lds(), s>>>(
-        a.logits, a.T, a.E, a.k, a.tpb, a.idx, a.w, a.hist, a.ded, a.R, a.per);
+        a.logits, a.T, a.E, a.k, a.tpb, a.idx, a.w, a.hist, a.ded, a.R, a.per, a.lead);
   else
     route_topk_kernel<L, V, kRouteThreads><<<a.nblk, kRouteThreads, a.lds(), s>>>(
-        a.logits, a.T, a.E, a.k, a.tpb, a.idx, a.w, a.hist, a.ded, a.R, a.per);
+        a.logits, a.T, a.E, a.k, a.tpb, a.idx, a.w, a.hist, a.ded, a.R, a.per, a.lead);
   return hipGetLastError();
 }
 
@@ -334,7 +347,7 @@ template <int V, int NT>
 hipError_t launch_wave_nt(const TopkArgs& a, hipStream_t s) {
 #define MOE_WAVE(KP)                                                                    \
   route_topk_wave_kernel<V, KP, NT><<<a.nblk, NT, a.lds(), s>>>(                        \
-      a.logits, a.T, a.E, a.k, a.tpb, a.idx, a.w, a.hist, a.ded, a.R, a.per)
+      a.logits, a.T, a.E, a.k, a.tpb, a.idx, a.w, a.hist, a.ded, a.R, a.per, a.lead)
   if (a.k <= 1) MOE_WAVE(1);
   else if (a.k <= 2) MOE_WAVE(2);
   else if (a.k <= 4) MOE_WAVE(4);
@@ -403,8 +416,9 @@ Blocking blocking_for(int T, int E, int R) {
 size_t workspace_bytes(int T, int E, int R) {
   const Blocking b = blocking_for(T, E, R);
   // route rows [blocks, E], plus [blocks, R] of per-rank counts when the
-  // one-call plan takes them from the top-k kernel
-  const size_t route = (size_t)b.route_nblk * (E + R) * sizeof(int32_t);
+  // one-call plan takes them from the top-k kernel, plus T leader masks when
+  // the one-call single-send plan does
+  const size_t route = ((size_t)b.route_nblk * (E + R) + (size_t)T) * sizeof(int32_t);
   const size_t layout = ((size_t)b.layout_nblk * (E + R) + (size_t)T) * sizeof(int32_t);
   size_t n = route > layout ? route : layout;
   n = (n + 255) & ~(size_t)255;
@@ -421,13 +435,14 @@ size_t route_assign_layout_ws_bytes(int T, int E, int R) {
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
-                             int32_t* ws, hipStream_t s, int32_t* ded_rows, int R) {
+                             int32_t* ws, hipStream_t s, int32_t* ded_rows, int R,
+                             int32_t* lead) {
   if (T == 0) return hipSuccess;
   const Blocking b = blocking_for(T, E, 1);
   const int L = lanes_per_token(E);
   const int V = (E + L - 1) / L;  // L = 16: 1..4; 32: 3..4; 64: 3..16
   const TopkArgs a{logits, T, E, k, b.route_tpb, b.route_nblk, b.route_threads, idx, w, ws, ded_rows, R,
-                   ded_rows != nullptr ? E / R : 1};
+                   ded_rows != nullptr ? E / R : 1, ded_rows != nullptr ? lead : nullptr};
   if (L == 16 && V == 1) return launch_topk<16, 1>(a, s);
   if (L == 16 && V == 2) return launch_topk<16, 2>(a, s);
   if (L == 16) return launch_topk<16, 4>(a, s);

@@ -181,6 +181,15 @@ def layout_single_send(b: Buffers, ss: SingleSend, stream=None) -> None:
                              ss.ss_token, b.ws, stream)
 
 
+def route_assign_layout_single_send(b: Buffers, ss: SingleSend, stream=None) -> None:
+    """route, assign and the single-send layout in one library call (three
+    launches for a batch without a replica table)."""
+    B.moe_route_assign_layout_single_send(b.p, b.logits, b.rep, b.maxrep, b.idx, b.w, b.counts,
+                                          b.assign, b.active, b.rank_of, b.expert_offsets,
+                                          b.rank_offsets, b.pos, b.src, b.dedup,
+                                          ss.ss_rank_offsets, ss.ss_row, ss.ss_token, b.ws, stream)
+
+
 def single_send_dispatch(b: Buffers, ss: SingleSend, stream=None) -> None:
     B.moe_single_send_dispatch(b.p, b.x, ss.ss_row, ss.send_ss, stream)
 

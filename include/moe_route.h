@@ -109,9 +109,10 @@ const char* moe_status_string(int32_t status);
 /* Description of the last non-OK status returned on this thread ("" if none). */
 const char* moe_last_error(void);
 
-/* Bytes of device workspace moe_route, moe_layout and moe_layout_single_send
- * need for this problem (one buffer of this size serves all three; its
- * contents need no initialisation and are not meaningful between calls).
+/* Bytes of device workspace moe_route, moe_layout, moe_layout_single_send and
+ * the one-call plans need for this problem (one buffer of this size serves
+ * all of them; its contents need no initialisation and are not meaningful
+ * between calls).
  * Host only; enqueues nothing. */
 moe_status moe_workspace_bytes(const moe_problem* p, size_t* bytes);
 
@@ -215,6 +216,26 @@ moe_status moe_route_assign_layout(const moe_problem* p, const float* logits, co
                                    int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos,
                                    int32_t* src, int32_t* dedup, void* ws, size_t ws_bytes,
                                    void* stream);
+
+/* moe_route, moe_assign_replicas and moe_layout_single_send in one call, with
+ * the same arguments and outputs as those three calls made in that order:
+ * the routing and the plain layout, plus the single-send rows of a
+ * dispatcher that sends each token to a GPU once (news summary of correlated
+ * expert placement and token shuffling, section "Two locality techniques").
+ *   - a batch without a replica table (rep NULL): three launches, the top-k
+ *     kernel (which also counts each block's tokens per rank and records
+ *     each token's first slot on each of its ranks), a column scan, and one
+ *     launch for the permutation and the single-send rows;
+ *   - with a replica table, or T = 0: the kernels of the three calls.
+ *   ss_rank_offsets, ss_row, ss_token as for moe_layout_single_send (ss_row
+ *   and ss_token i32 [T*k], unused when T = 0).
+ * ws is one workspace of moe_workspace_bytes().                             */
+moe_status moe_route_assign_layout_single_send(
+    const moe_problem* p, const float* logits, const int32_t* rep, int32_t maxrep, int32_t* idx,
+    float* w, int32_t* counts, int32_t* assign, int32_t* active, int32_t* rank_of,
+    int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos, int32_t* src, int32_t* dedup,
+    int32_t* ss_rank_offsets, int32_t* ss_row, int32_t* ss_token, void* ws, size_t ws_bytes,
+    void* stream);
 
 /* Bytes of the static device scratch behind moe_route_assign_layout_noalloc
  * (2 MiB per GPU). */
