@@ -342,15 +342,24 @@ def warm_leg(P, b, steps, ev, np, torch, dc_bytes):
 
 def single_send_leg(P, w, b, flush, steps, ev, np, torch):
     """The single-send variant on the same batch, timed after the headline
-    loop: its layout (the plain layout plus the single-send rows), the
-    dispatch of one row per (token, destination rank), and the receiver
-    fan-out back to the expert-grouped buffer, each cold-cache like the
-    headline. Algorithmic bytes: dispatch (T + n_ss) H b, fan-out
+    loop: route, assignment and single-send layout in one call
+    (`one_call_plan`), the single-send layout call alone (the plain layout
+    plus the single-send rows), the dispatch of one row per (token,
+    destination rank), and the receiver fan-out back to the expert-grouped
+    buffer, each cold-cache like the headline. Algorithmic bytes: dispatch (T + n_ss) H b, fan-out
     (n_ss + T k) H b (each single-send row read once, every expert row
     written once)."""
     ss = P.allocate_single_send(b)
-    marks = []
+    marks, plan_marks = [], []
     for i in range(steps + 2):
+        # route, assignment and single-send layout in one call, enqueued
+        # behind a flush so the bracket holds kernel time
+        if flush is not None:
+            flush.fill_(14.0)
+        p0, p1 = ev(), ev()
+        p0.record()
+        P.route_assign_layout_single_send(b, ss)
+        p1.record()
         e = [ev() for _ in range(6)]
         e[0].record()
         P.layout_single_send(b, ss)
@@ -367,17 +376,19 @@ def single_send_leg(P, w, b, flush, steps, ev, np, torch):
         e[5].record()
         if i >= 2:
             marks.append(e)
+            plan_marks.append((p0, p1))
     torch.cuda.synchronize()
     avg = lambda i: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks]))
     lay_ms, dsp_ms, exp_ms = avg(0), avg(2), avg(4)
+    plan_ms = float(np.mean([a.elapsed_time(c) for a, c in plan_marks]))
     n_ss = int(ss.ss_rank_offsets[-1].item())
     rb = w.H * 2
     d_bytes = (w.T + n_ss) * rb
     x_bytes = (n_ss + w.T * w.k) * rb
     return {"rows": n_ss, "raw_rows": w.T * w.k, "rows_cut_frac": round(1 - n_ss / (w.T * w.k), 4),
             "steps": steps,
-            "stage_ms": {"layout": round(lay_ms, 4), "dispatch": round(dsp_ms, 4),
-                         "expand": round(exp_ms, 4)},
+            "stage_ms": {"one_call_plan": round(plan_ms, 4), "layout": round(lay_ms, 4),
+                         "dispatch": round(dsp_ms, 4), "expand": round(exp_ms, 4)},
             "dispatch_GBps": round(d_bytes / (dsp_ms / 1e3) / 1e9, 1),
             "expand_GBps": round(x_bytes / (exp_ms / 1e3) / 1e9, 1),
             "dispatch_bytes": d_bytes, "expand_bytes": x_bytes}
