@@ -65,7 +65,8 @@ def test_graph_of_every_entry_point(w):
     """The forward pass, the single-send layout, dispatch and fan-out, the
     backward of combine and dispatch, the routing statistics (cleared by a
     fill kernel, not a memset), the token-balanced split and the one-call
-    route + assignment + layout, all recorded in one graph: three replays, with the outputs overwritten between them,
+    route + assignment + layout (with and without the single-send rows),
+    all recorded in one graph: three replays, with the outputs overwritten between them,
     each equal bit for bit to the eager pass."""
     from combine_router_topk_amd import binding as B
     say(f"[case] graph of every entry point {w.name}")
@@ -89,6 +90,7 @@ def test_graph_of_every_entry_point(w):
         lambda b_: P.routing_stats(b_, st),
         lambda b_: P.token_balanced_split(b_, sp),
         P.route_assign_layout,  # rewrites the routing outputs with the same values
+        lambda b_: P.route_assign_layout_single_send(b_, ss),  # and the single-send rows
     )
     for step in steps[len(P.STEPS):]:
         step(b)

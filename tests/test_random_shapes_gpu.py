@@ -22,6 +22,7 @@ from test_backward_gpu import run_backward
 from test_eplb_gpu import random_table, run_split
 from test_fused_plan_gpu import run_both
 from test_parity_gpu import run_and_check
+from test_fused_single_send_gpu import run_both as run_both_ss
 from test_single_send_gpu import check_single_send, run_single_send
 from test_stats_gpu import run_stats
 
@@ -101,6 +102,8 @@ def test_random_problem_every_entry_point(c):
     run_and_check(w, flags=flags, rep=rep, order=order, logits=logits, x=x)
     # route, assign and layout as one call: equal to the separate calls
     run_both(w, rep=rep, order=order, logits=logits)
+    # and with the single-send rows
+    run_both_ss(w, rep=rep, order=order, logits=logits)
     # single-send layout, dispatch and fan-out
     b, ss, expanded = run_single_send(w, logits, x, rep, flags)
     ref = oracle.route_and_layout(w.T, w.E, w.k, w.R, logits, rep, order)
