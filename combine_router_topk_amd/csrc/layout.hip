@@ -908,12 +908,15 @@ __device__ __forceinline__ int popc_words(const unsigned long long* row, int W) 
   return c;
 }
 
-__host__ __device__ constexpr int mask_plan_ints(int T, int E, int k, int R) {
+// LDS ints of route_plan_mask_kernel; with ss, room for the single-send rows
+// (at most 64 ranks).
+__host__ __device__ constexpr int mask_plan_ints(int T, int E, int k, int R, bool ss = false) {
   const int W = (T + 63) / 64, e8 = (E + 8) & ~7;
   return round4(2 * W * E) + 2 * round4(e8) + 2 * round4(E) + 3 * round4(R) +
          round4(R > kWave ? R : kWave) + round4((E + 3) / 4) + round4(E * kMaxRep / 2) +
          2 * round4((T * k + 1) / 2) +
-         (R <= kWave ? round4(kPlanWaves * R) + round4(R + 1) + 2 * round4(E) + 2 * kWave : 0);
+         (R <= kWave ? round4(kPlanWaves * R) + round4(R + 1) + 2 * round4(E) + 2 * kWave : 0) +
+         (ss && R <= kWave ? round4(kPlanWaves * R) + round4(R) : 0);
 }
 
 // The destination ranks of one token's k slots as a 64-bit set (ranks < 64):
@@ -975,14 +978,18 @@ __device__ __forceinline__ void finish_few_ranks(
     int T, int E, int k, int R, const int* s_rank, const int* s_counts,
     const unsigned short* s_idx, int* s_ded, int* s_wr, int* s_rbase, int* s_ord, int* s_scan,
     int* s_eoff, int* s_wave, int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
-    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ dedup) {
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ dedup, int* s_ssw = nullptr,
+    int* s_ssoff = nullptr, int32_t* __restrict__ ss_rank_offsets = nullptr,
+    int32_t* __restrict__ ss_row = nullptr, int32_t* __restrict__ ss_token = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  if (wave < (T + kWave - 1) / kWave) {  // uniform per wave
+  const bool ss = ss_rank_offsets != nullptr;  // uniform: an argument
+  const int n_tw = (T + kWave - 1) / kWave;     // waves holding tokens
+  unsigned long long rm = 0ull;                 // this thread's token's ranks
+  if (wave < n_tw) {  // uniform per wave
     // the token's ids are read with loads issued together (in a bucket of
     // 4, 8 or 16 slots; slots past k reread slot k - 1), then their ranks
-    unsigned long long rm = 0ull;
     if (tid < T) {
       const unsigned short* row = s_idx + tid * k;
       rm = k <= 4 ? token_rank_set<4>(row, k, s_rank)
@@ -996,6 +1003,7 @@ __device__ __forceinline__ void finish_few_ranks(
       cnt = lane == r ? c : cnt;
     }
     if (lane < R && cnt > 0) atomicAdd(&s_ded[lane], cnt);
+    if (ss && lane < R) s_ssw[wave * R + lane] = cnt;  // the wave's tokens per rank
   }
   const int r = tid < E ? s_rank[tid] : R;  // R: past every rank
   const int nbits = 32 - __builtin_clz(static_cast<unsigned>(R));
@@ -1013,9 +1021,18 @@ __device__ __forceinline__ void finish_few_ranks(
     if (lane < R)
       for (int w = 0; w < kPlanWaves; ++w) ne += s_wr[w * R + lane];
     const int incl = wave_incl_scan(ne, lane);
+    const int nd = lane < R ? s_ded[lane] : 0;
     if (lane < R) {
       s_rbase[lane] = incl - ne;
-      dedup[lane] = s_ded[lane];
+      dedup[lane] = nd;
+    }
+    if (ss) {  // single-send offsets: the dedup totals scanned over ranks
+      const int incl_d = wave_incl_scan(nd, lane);
+      if (lane < R) {
+        s_ssoff[lane] = incl_d - nd;
+        ss_rank_offsets[lane] = incl_d - nd;
+      }
+      if (lane == kWave - 1) ss_rank_offsets[R] = incl_d;
     }
   }
   __syncthreads();
@@ -1046,6 +1063,37 @@ __device__ __forceinline__ void finish_few_ranks(
   }
   if (tid < R) rank_offsets[tid] = s_rbase[tid] < E ? s_scan[s_rbase[tid]] : total;
   if (tid == 0) rank_offsets[R] = total;
+  if (ss && wave < n_tw) {  // uniform per wave
+    // single-send rows: for rank r the tokens holding it, in token order;
+    // this token's row is the rank's offset, plus the earlier waves'
+    // tokens on r (lane r of `pre`), plus the lower lanes on r (a ballot)
+    int pre = 0;
+    if (lane < R)
+      for (int w = 0; w < wave; ++w) pre += s_ssw[w * R + lane];
+    int rk[kMaxK];
+    if (tid < T) {
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) rk[j] = j < k ? s_rank[s_idx[tid * k + j]] : -1;
+    }
+    const uint64_t lt = lanemask_lt(lane);
+    for (int q = 0; q < R; ++q) {
+      const bool on = (rm >> q) & 1ull;
+      const uint64_t br = ballot(on);
+      const int before = __builtin_amdgcn_readlane(pre, q);
+      if (on) {
+        const int row = s_ssoff[q] + before + __popcll(br & lt);
+        bool first = true;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+          if (j < k && rk[j] == q) {
+            ss_row[(size_t)tid * k + j] = row;
+            if (first) ss_token[row] = tid;
+            first = false;
+          }
+        }
+      }
+    }
+  }
   __syncthreads();
 }
 
@@ -1055,7 +1103,8 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
     int32_t* __restrict__ counts, int32_t* __restrict__ assign, int32_t* __restrict__ active,
     int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pos, int32_t* __restrict__ src,
-    int32_t* __restrict__ dedup) {
+    int32_t* __restrict__ dedup, int32_t* __restrict__ ss_rank_offsets,
+    int32_t* __restrict__ ss_row, int32_t* __restrict__ ss_token) {
   extern __shared__ __align__(16) int smem[];
   __shared__ int s_wave[kPlanWaves];
   __shared__ int s_wave2[kPlanWaves];
@@ -1087,6 +1136,9 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
   int* s_ord = p;   p += few ? round4(E) : 0;
   int* s_scan = p;  p += few ? round4(E) : 0;
   unsigned long long* adj = reinterpret_cast<unsigned long long*>(p);  // [64] when few
+  p += few ? 2 * kWave : 0;
+  int* s_ssw = p;   p += few ? round4(kPlanWaves * R) : 0;  // single-send rows (with ss outputs)
+  int* s_ssoff = p;
 
   // every global load first, all in flight together: expert ids and replica
   // rows. Each load reads an index clamped into its array (T, k, maxrep >= 1
@@ -1225,7 +1277,8 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
   __syncthreads();
   if (few) {
     finish_few_ranks(T, E, k, R, s_rank, s_counts, s_idx, s_ded, s_wr, s_rbase, s_ord, s_scan,
-                     s_eoff, s_wave, rank_of, expert_offsets, rank_offsets, dedup);
+                     s_eoff, s_wave, rank_of, expert_offsets, rank_offsets, dedup, s_ssw, s_ssoff,
+                     ss_rank_offsets, ss_row, ss_token);
   } else {
     if (tid < T) {  // distinct destination ranks of the token
       int rk[kMaxK];
@@ -1327,7 +1380,7 @@ hipError_t launch_route_assign_layout(const float* logits, int T, int E, int k, 
     route_plan_mask_kernel<<<1, kPlanThreads, mask_plan_ints(T, E, k, R) * sizeof(int), s>>>(
         idx, T, E, k, R, rep, rep ? maxrep : 1,
         id_order ? 1 : 0, counts, assign, active, rank_of, expert_offsets, rank_offsets, pos, src,
-        dedup);
+        dedup, nullptr, nullptr, nullptr);
     return hipGetLastError();
   }
   if (T > 0 && (int64_t)T * k <= kSmallPairs && plan_ints <= kSmallLdsInts) {
@@ -1375,6 +1428,17 @@ hipError_t launch_route_assign_layout_single_send(
     int32_t* idx, float* w, int32_t* counts, int32_t* assign, int32_t* active, int32_t* rank_of,
     int32_t* expert_offsets, int32_t* rank_offsets, int32_t* pos, int32_t* src, int32_t* dedup,
     int32_t* ss_rank_offsets, int32_t* ss_row, int32_t* ss_token, int32_t* ws, hipStream_t s) {
+  if (T > 0 && T <= kMaskMaxT && (int64_t)T * k <= kSmallPairs && R <= kWave &&
+      mask_plan_ints(T, E, k, R, true) <= kSmallLdsInts) {
+    // a decode-sized batch: the top-k kernel, then one workgroup that also
+    // lays out the single-send rows (by ballots over each rank's tokens)
+    hipError_t err = launch_route_topk(logits, T, E, k, idx, w, nullptr, s);
+    if (err != hipSuccess) return err;
+    route_plan_mask_kernel<<<1, kPlanThreads, mask_plan_ints(T, E, k, R, true) * sizeof(int), s>>>(
+        idx, T, E, k, R, rep, rep ? maxrep : 1, id_order ? 1 : 0, counts, assign, active, rank_of,
+        expert_offsets, rank_offsets, pos, src, dedup, ss_rank_offsets, ss_row, ss_token);
+    return hipGetLastError();
+  }
   if (rep == nullptr && T > 0) {
     // no replica table: top-k with per-block counts and leader masks, the
     // column scan (expert and rank columns to prefixes), then the

@@ -222,11 +222,16 @@ moe_status moe_route_assign_layout(const moe_problem* p, const float* logits, co
  * the routing and the plain layout, plus the single-send rows of a
  * dispatcher that sends each token to a GPU once (news summary of correlated
  * expert placement and token shuffling, section "Two locality techniques").
- *   - a batch without a replica table (rep NULL): three launches, the top-k
- *     kernel (which also counts each block's tokens per rank and records
- *     each token's first slot on each of its ranks), a column scan, and one
- *     launch for the permutation and the single-send rows;
- *   - with a replica table, or T = 0: the kernels of the three calls.
+ *   - a batch with T <= 1024, T*k <= 8192 and R <= 64 whose tables fit in
+ *     64 KiB of LDS: two launches, the top-k kernel, then one workgroup that
+ *     sums the demand vector, runs the greedy and lays out the batch and its
+ *     single-send rows;
+ *   - a larger batch without a replica table (rep NULL): three launches, the
+ *     top-k kernel (which also counts each block's tokens per rank and
+ *     records each token's first slot on each of its ranks), a column scan,
+ *     and one launch for the permutation and the single-send rows;
+ *   - otherwise (a larger batch with a replica table, or T = 0): the kernels
+ *     of the three calls.
  *   ss_rank_offsets, ss_row, ss_token as for moe_layout_single_send (ss_row
  *   and ss_token i32 [T*k], unused when T = 0).
  * ws is one workspace of moe_workspace_bytes().                             */

@@ -2,10 +2,12 @@
 greedy assignment + single-send layout: on every shape its outputs equal,
 bit for bit, those of moe_route, moe_assign_replicas and
 moe_layout_single_send called in turn, and the oracle's (the routing, the
-plain layout and the single-send offsets, rows and row tokens). Batches
-without a replica table take the three-launch path (top-k with per-rank
-counts and leader masks, column scan, permutation + single-send rows); with
-a table, and for T = 0, the three calls' kernels."""
+plain layout and the single-send offsets, rows and row tokens). Decode-sized
+batches with at most 64 ranks take the two-launch path (top-k, then one
+workgroup that also lays out the single-send rows); larger batches without a
+replica table the three-launch path (top-k with per-rank counts and leader
+masks, column scan, permutation + single-send rows); larger batches with a
+table, and T = 0, the three calls' kernels."""
 import numpy as np
 import pytest
 import torch
@@ -88,6 +90,12 @@ def test_decode_table_id_order():
     run_both(synth.DECODE, 0, order="id")
 
 
+def test_decode_table_larger_batch():
+    """1024 tokens with the decode replica table: past one workgroup's LDS,
+    so the three calls' kernels."""
+    run_both(synth.scaled(synth.DECODE, T=1024, H=8), 1)
+
+
 @pytest.mark.parametrize("w", [synth.TRAIN_TOP2, synth.TRAIN_TOP6,
                                synth.scaled(synth.LARGE, T=40000, H=8)], ids=lambda w: w.name)
 def test_full_size_batches(w):
@@ -105,6 +113,8 @@ EDGE = [
     ("E64_k8_R64_T5000", 5000, 64, 8, 64),
     ("E96_k4_R96_T20000", 20000, 96, 4, 96),   # rank columns past one 64-column task
     ("T1", 1, 64, 2, 32),
+    ("E64_k4_R64_T1000", 1000, 64, 4, 64),    # one workgroup, 64 ranks (ballot lanes all used)
+    ("E1024_k2_R32_T1000", 1000, 1024, 2, 32),  # masks too large for one workgroup: three launches
 ]
 
 
