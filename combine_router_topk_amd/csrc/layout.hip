@@ -916,7 +916,7 @@ __host__ __device__ constexpr int mask_plan_ints(int T, int E, int k, int R, boo
          round4(R > kWave ? R : kWave) + round4((E + 3) / 4) + round4(E * kMaxRep / 2) +
          2 * round4((T * k + 1) / 2) +
          (R <= kWave ? round4(kPlanWaves * R) + round4(R + 1) + 2 * round4(E) + 2 * kWave : 0) +
-         (ss && R <= kWave ? round4(kPlanWaves * R) + round4(R) : 0);
+         (ss && R <= kWave ? 2 * round4(kPlanWaves * R) + round4(R) + 2 * kPlanWaves * R : 0);
 }
 
 // The destination ranks of one token's k slots as a 64-bit set (ranks < 64):
@@ -979,8 +979,9 @@ __device__ __forceinline__ void finish_few_ranks(
     const unsigned short* s_idx, int* s_ded, int* s_wr, int* s_rbase, int* s_ord, int* s_scan,
     int* s_eoff, int* s_wave, int32_t* __restrict__ rank_of, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ dedup, int* s_ssw = nullptr,
-    int* s_ssoff = nullptr, int32_t* __restrict__ ss_rank_offsets = nullptr,
-    int32_t* __restrict__ ss_row = nullptr, int32_t* __restrict__ ss_token = nullptr) {
+    int* s_ssoff = nullptr, int* s_ssbase = nullptr, uint64_t* s_ssb = nullptr,
+    int32_t* __restrict__ ss_rank_offsets = nullptr, int32_t* __restrict__ ss_row = nullptr,
+    int32_t* __restrict__ ss_token = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -999,8 +1000,9 @@ __device__ __forceinline__ void finish_few_ranks(
     // then one LDS add per rank)
     int cnt = 0;
     for (int r = 0; r < R; ++r) {
-      const int c = __popcll(ballot((rm >> r) & 1ull));
-      cnt = lane == r ? c : cnt;
+      const uint64_t br = ballot((rm >> r) & 1ull);
+      cnt = lane == r ? __popcll(br) : cnt;
+      if (ss && lane == 0) s_ssb[wave * R + r] = br;  // the wave's tokens on rank r
     }
     if (lane < R && cnt > 0) atomicAdd(&s_ded[lane], cnt);
     if (ss && lane < R) s_ssw[wave * R + lane] = cnt;  // the wave's tokens per rank
@@ -1044,6 +1046,12 @@ __device__ __forceinline__ void finish_few_ranks(
     s_ord[place] = s_counts[tid];
     rank_of[tid] = r;
   }
+  if (ss && tid < n_tw * R) {  // wave w's first single-send row on rank q
+    const int w = tid / R, q = tid - w * R;
+    int base = s_ssoff[q];
+    for (int v = 0; v < w; ++v) base += s_ssw[v * R + q];
+    s_ssbase[tid] = base;
+  }
   __syncthreads();
   // one wave scans the counts in (rank, id) order, P = ceil(E / 64) per
   // lane; lane 63's inclusive sum is the total
@@ -1063,35 +1071,20 @@ __device__ __forceinline__ void finish_few_ranks(
   }
   if (tid < R) rank_offsets[tid] = s_rbase[tid] < E ? s_scan[s_rbase[tid]] : total;
   if (tid == 0) rank_offsets[R] = total;
-  if (ss && wave < n_tw) {  // uniform per wave
-    // single-send rows: for rank r the tokens holding it, in token order;
-    // this token's row is the rank's offset, plus the earlier waves'
-    // tokens on r (lane r of `pre`), plus the lower lanes on r (a ballot)
-    int pre = 0;
-    if (lane < R)
-      for (int w = 0; w < wave; ++w) pre += s_ssw[w * R + lane];
-    int rk[kMaxK];
-    if (tid < T) {
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) rk[j] = j < k ? s_rank[s_idx[tid * k + j]] : -1;
-    }
+  if (ss && tid < T) {
+    // single-send rows: for rank q the tokens holding it, in token order; a
+    // slot's row is its wave's first row on q plus the lower lanes holding q
+    // (from the wave's ballot); the token's first slot on q writes the row's
+    // token
     const uint64_t lt = lanemask_lt(lane);
-    for (int q = 0; q < R; ++q) {
-      const bool on = (rm >> q) & 1ull;
-      const uint64_t br = ballot(on);
-      const int before = __builtin_amdgcn_readlane(pre, q);
-      if (on) {
-        const int row = s_ssoff[q] + before + __popcll(br & lt);
-        bool first = true;
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-          if (j < k && rk[j] == q) {
-            ss_row[(size_t)tid * k + j] = row;
-            if (first) ss_token[row] = tid;
-            first = false;
-          }
-        }
-      }
+    const unsigned short* row_ids = s_idx + tid * k;
+    for (int j = 0; j < k; ++j) {
+      const int q = s_rank[row_ids[j]];
+      const int row = s_ssbase[wave * R + q] + __popcll(s_ssb[wave * R + q] & lt);
+      ss_row[(size_t)tid * k + j] = row;
+      bool first = true;
+      for (int jj = 0; jj < j; ++jj) first &= s_rank[row_ids[jj]] != q;
+      if (first) ss_token[row] = tid;
     }
   }
   __syncthreads();
@@ -1137,8 +1130,13 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
   int* s_scan = p;  p += few ? round4(E) : 0;
   unsigned long long* adj = reinterpret_cast<unsigned long long*>(p);  // [64] when few
   p += few ? 2 * kWave : 0;
-  int* s_ssw = p;   p += few ? round4(kPlanWaves * R) : 0;  // single-send rows (with ss outputs)
-  int* s_ssoff = p;
+  // single-send rows (used only with the single-send outputs): per-wave
+  // token counts and first rows per rank, the rank offsets, and each wave's
+  // ballot of its tokens on each rank
+  int* s_ssw = p;    p += few ? round4(kPlanWaves * R) : 0;
+  int* s_ssbase = p; p += few ? round4(kPlanWaves * R) : 0;
+  int* s_ssoff = p;  p += few ? round4(R) : 0;
+  uint64_t* s_ssb = reinterpret_cast<uint64_t*>(p);  // [kPlanWaves][R]
 
   // every global load first, all in flight together: expert ids and replica
   // rows. Each load reads an index clamped into its array (T, k, maxrep >= 1
@@ -1278,7 +1276,7 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_mask_kernel(
   if (few) {
     finish_few_ranks(T, E, k, R, s_rank, s_counts, s_idx, s_ded, s_wr, s_rbase, s_ord, s_scan,
                      s_eoff, s_wave, rank_of, expert_offsets, rank_offsets, dedup, s_ssw, s_ssoff,
-                     ss_rank_offsets, ss_row, ss_token);
+                     s_ssbase, s_ssb, ss_rank_offsets, ss_row, ss_token);
   } else {
     if (tid < T) {  // distinct destination ranks of the token
       int rk[kMaxK];
