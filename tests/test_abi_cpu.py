@@ -183,7 +183,17 @@ def test_new_entry_points_empty_batch_is_noop_where_nothing_is_written():
 def test_plain_c_caller_builds_and_exports_its_check():
     from conftest import C_CHECK_LIB
     lib = ctypes.CDLL(C_CHECK_LIB)
-    assert hasattr(lib, "moe_c_abi_check")
+    assert hasattr(lib, "moe_c_abi_check") and hasattr(lib, "moe_c_abi_check_rest")
+
+
+def test_plain_c_caller_calls_every_compute_entry_point():
+    """Every call of the header that enqueues work is made from plain C."""
+    header = open(HEADER).read()
+    calls = set(re.findall(r"^moe_status (moe_\w+)\(", header, re.M)) - {"moe_workspace_bytes"}
+    assert len(calls) >= 16
+    src = open(os.path.join(ROOT, "tests", "c_abi", "check_abi.c")).read()
+    missing = sorted(c for c in calls if not re.search(rf"\b{c}\(", src))
+    assert not missing, missing
 
 
 def test_binding_limits_match_header():
