@@ -83,6 +83,21 @@ __device__ __forceinline__ void declare_lds_reserve(int never_negative) {
   if (never_negative < 0) lds_reserve[threadIdx.x] = 0;
 }
 
+// Row slices: wide rows are cut into slices of kSliceChunks 16-byte chunks,
+// one 128-thread block per slice and one chunk per lane. Block b of a launch
+// whose first row is `first` takes slice b mod S of row first + b / S (S
+// slices per row), so the slices of a row are dispatched together; c is the
+// lane's chunk in the row (at most S * kSliceChunks - 1: lanes past the row
+// end hold no chunk).
+constexpr int kSliceChunks = 128;
+__host__ __device__ constexpr int slices_per_row(int cpr) { return (cpr + kSliceChunks - 1) / kSliceChunks; }
+
+__device__ __forceinline__ void slice_of_block(int S, int first, int& row, int& c) {
+  const int rr = static_cast<int>(blockIdx.x) / S;
+  row = first + rr;
+  c = (static_cast<int>(blockIdx.x) - rr * S) * kSliceChunks + static_cast<int>(threadIdx.x);
+}
+
 // ---- order-preserving keys for top-k ---------------------------------------
 // Larger key = better logit. Finite values and +-inf map monotonically into
 // [0x007fffff, 0xff800000]; -0.0 is folded onto +0.0 so the two tie; any NaN

@@ -260,6 +260,49 @@ __global__ __launch_bounds__(kGradThreads) void dispatch_backward_kernel(
   }
 }
 
+// dx over row slices (rows over 256 chunks): a block sums one 128-chunk
+// slice of each of the token's k rows, with the arithmetic of
+// dispatch_backward_kernel.
+template <int ACT, int KMAX, bool OUT_F32>
+__global__ __launch_bounds__(kSliceChunks) void dispatch_backward_slice_kernel(
+    const u32x4* __restrict__ dsend, const int32_t* __restrict__ pos, void* __restrict__ dx, int T,
+    int k, int cpr, int S, int first) {
+  declare_lds_reserve(cpr);
+  int t, c;
+  slice_of_block(S, first, t, c);
+  const int n_rows = T * k;
+  size_t row[KMAX];
+  bool ok[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    ok[j] = false;
+    row[j] = 0;
+    if (j < k) {
+      const int r = pos[(size_t)t * k + j];
+      ok[j] = static_cast<unsigned>(r) < static_cast<unsigned>(n_rows);
+      row[j] = ok[j] ? (size_t)r * cpr : 0;
+    }
+  }
+  if (c >= cpr) return;
+  u32x4 v[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (j < k && ok[j]) v[j] = __builtin_nontemporal_load(dsend + row[j] + c);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k && ok[j]) {
+      float f[8];
+      unpack8<ACT>(as_uint4(v[j]), f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += f[i];
+    }
+  }
+  grad_store<ACT, OUT_F32>(dx, (size_t)t * cpr + c, acc);
+}
+
 int grad_threads_per_row(int cpr) {
   int tpt = 16;
   while (tpt < cpr && tpt < kWave) tpt *= 2;
@@ -301,27 +344,43 @@ hipError_t launch_cb_k(const u32x4* dout, const u32x4* y, const int32_t* pos, co
   return launch_cb<ACT, 16>(dout, y, pos, w, dy, dw, T, k, cpr, s);
 }
 
-// LDS reservation of the one-row dispatch backward (see if_many_blocks),
-// from cold-cache sweeps on MI355X over H = 2048, 4096, 7168 and k = 2..8:
-// rows over 256 chunks take 48 KiB at k = 3..4 (6-12% over none) and 32 KiB
-// otherwise (7-9% at H = 7168, 1.5-7% at H = 4096); rows of 256 chunks or
-// fewer were fastest with none.
-size_t dispatch_backward_reserve(int k, int cpr) {
-  if (cpr <= 256) return 0;
-  return (k >= 3 && k <= 4 ? 48 : 32) * kKiB;
+// The dispatch backward cuts rows over 256 chunks into slices
+// (dispatch_backward_slice_kernel) in launches of at least kMinBlocksToCap
+// slices; shorter rows, and smaller launches, keep one-row blocks, fastest
+// with no LDS reservation. The slices' reservation grows
+// with k, which sets the row loads in flight per block: none at k <= 2,
+// 4 KiB at k = 3, 16 KiB at k = 4..6, 24 KiB above. Against one-row blocks
+// with their best reservations (cold cache, T = 16384, E = 64 unless
+// named): T = 65536, E = 256, k = 8, H = 7168: 1.37 against 1.52 ms;
+// H = 7168, k = 8: 331 against 379 us; k = 2: 110 against 118 us;
+// H = 4096, k = 2: 67.4 against 69.2 us; k = 3: 84.1 against 92.5 us;
+// k = 4: 108 against 111 us; k = 6: 152 against 165 us; H = 3072, k = 2:
+// 50.8 against 57.1 us; k = 8: 152 against 166 us.
+bool dispatch_backward_sliced(int T, int cpr) {
+  return cpr > 256 && enough_slices(T, slices_per_row(cpr));
+}
+size_t dispatch_backward_slice_reserve(int k) {
+  if (k <= 2) return 0;
+  if (k == 3) return 4 * kKiB;
+  return (k <= 6 ? 16 : 24) * kKiB;
 }
 
 template <int ACT, int KMAX, bool OUT_F32>
 hipError_t launch_db(const u32x4* dsend, const int32_t* pos, void* dx, int T, int k, int cpr,
                      hipStream_t s) {
-  if (cpr >= kGradOneRowChunks) {
-    const size_t res = if_many_blocks(dispatch_backward_reserve(k, cpr), T);
-    if (cpr <= 256)
-      dispatch_backward_kernel<ACT, KMAX, OUT_F32, true, true><<<T, kGradThreads, res, s>>>(
-          dsend, pos, dx, T, k, cpr, kGradThreads);
-    else
-      dispatch_backward_kernel<ACT, KMAX, OUT_F32, true, false><<<T, kGradThreads, res, s>>>(
-          dsend, pos, dx, T, k, cpr, kGradThreads);
+  if (dispatch_backward_sliced(T, cpr)) {
+    const int S = slices_per_row(cpr);
+    const size_t res = if_many_blocks(dispatch_backward_slice_reserve(k), (long long)T * S);
+    slice_launches(T, S, [&](int first, unsigned blocks) {
+      dispatch_backward_slice_kernel<ACT, KMAX, OUT_F32><<<blocks, kSliceChunks, res, s>>>(
+          dsend, pos, dx, T, k, cpr, S, first);
+    });
+  } else if (cpr >= kGradOneRowChunks && cpr <= 256) {
+    dispatch_backward_kernel<ACT, KMAX, OUT_F32, true, true><<<T, kGradThreads, 0, s>>>(
+        dsend, pos, dx, T, k, cpr, kGradThreads);
+  } else if (cpr > 256) {
+    dispatch_backward_kernel<ACT, KMAX, OUT_F32, true, false><<<T, kGradThreads, 0, s>>>(
+        dsend, pos, dx, T, k, cpr, kGradThreads);
   } else {
     const int tpt = grad_threads_per_row(cpr);
     const int per_blk = kGradThreads / tpt;

@@ -51,10 +51,7 @@ __device__ __forceinline__ void row_team(int tpt, int& row, int& lane, int& stri
 }
 
 // Each lane loads its U chunks of the token row, then stores them to the
-// row's k send rows. With SERIAL, each load completes before the next is
-// issued: for long rows with many copies (H = 7168, k = 8: 56 stores per
-// lane) this staggers the waves' store bursts and measured 7% faster
-// (1.63 vs 1.76 ms); for shorter rows it does not help.
+// row's k send rows.
 //
 // With SS (single-send dispatch), pos is the token's single-send row per slot
 // and n_rows the buffer's row capacity; a row shared by several slots (the
@@ -69,7 +66,7 @@ __device__ __forceinline__ void row_team(int tpt, int& row, int& lane, int& stri
 // 75.5 against 69.2 us, and no LDS reservation from 0 to 64 KiB recovers
 // it): the stores then start sooner and more scattered write streams are
 // open at once. At H = 7168 it made no difference.
-template <int NT, int U, bool ONE, bool SERIAL = false, bool SS = false, bool PREF = false>
+template <int NT, int U, bool ONE, bool SS = false, bool PREF = false>
 __global__ __launch_bounds__(NT) void dispatch_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ send, int T,
     int k, int cpr, int tpt, int capacity = 0) {
@@ -98,7 +95,6 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * stride;
       if (c < cpr) v[u] = __builtin_nontemporal_load(xr + c);
-      if constexpr (SERIAL) __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     if constexpr (SS) {
       if (c0 == lt) {
@@ -126,12 +122,34 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(
   }
 }
 
-// U > 1: up to U chunks per lane are loaded before the row's expert id (two
+// Wide rows, one block per row slice (slice_of_block): each block reads
+// 2 KiB of a token's row and writes it to the token's k send rows; SS and
+// the bad-row skip as in dispatch_kernel.
+template <bool SS>
+__global__ __launch_bounds__(kSliceChunks) void dispatch_slice_kernel(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ send, int k,
+    int cpr, int S, int first, int n_rows) {
+  declare_lds_reserve(cpr);
+  int t, c;
+  slice_of_block(S, first, t, c);
+  const int32_t* pr = pos + (size_t)t * k;
+  u32x4 v;
+  if (c < cpr) v = __builtin_nontemporal_load(x + (size_t)t * cpr + c);
+  for (int j = 0; j < k; ++j) {
+    const int r = pr[j];
+    if (static_cast<unsigned>(r) >= static_cast<unsigned>(n_rows)) continue;  // bad pos: skipped
+    if constexpr (SS) {
+      bool dup = false;  // an earlier slot carries this row
+      for (int jj = 0; jj < j; ++jj) dup |= (pr[jj] == r);
+      if (dup) continue;
+    }
+    if (c < cpr) __builtin_nontemporal_store(v, send + (size_t)r * cpr + c);
+  }
+}
+
+// Up to U chunks per lane are loaded before the row's expert id (two
 // dependent loads: src, then idx) is looked up, so the id's latency overlaps
 // the row loads (H = 2048, k = 6: 125 against 139 us; H = 4096: 2% less).
-// U == 1 (rows of more than 512 chunks): the id first, then one chunk at a
-// time; batching the loads there measured 11% slower (H = 7168, k = 8:
-// 2.61 against 2.35 ms).
 template <int ACT, bool ONE, int U>
 __global__ __launch_bounds__(kRowThreads) void standin_kernel(
     const u32x4* send, const int32_t* __restrict__ src, const int32_t* __restrict__ idx, u32x4* y,
@@ -154,26 +172,45 @@ __global__ __launch_bounds__(kRowThreads) void standin_kernel(
     for (int i = 0; i < 8; ++i) f[i] = keep_f32(f[i] * scale);  // product rounded to fp32
     __builtin_nontemporal_store(to_vec(pack8<ACT>(f)), out + c);
   };
-  if constexpr (U == 1) {
-    const float scale = expert_scale();
-    for (int c = lt; c < cpr; c += stride) convert(__builtin_nontemporal_load(in + c), scale, c);
-  } else {
-    float scale = 0.0f;
-    for (int c0 = lt; c0 < cpr; c0 += stride * U) {
-      u32x4 v[U];
+  float scale = 0.0f;
+  for (int c0 = lt; c0 < cpr; c0 += stride * U) {
+    u32x4 v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * stride;
-        if (c < cpr) v[u] = __builtin_nontemporal_load(in + c);
-      }
-      if (c0 == lt) scale = expert_scale();
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * stride;
-        if (c >= cpr) break;
-        convert(v[u], scale, c);
-      }
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * stride;
+      if (c < cpr) v[u] = __builtin_nontemporal_load(in + c);
     }
+    if (c0 == lt) scale = expert_scale();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * stride;
+      if (c >= cpr) break;
+      convert(v[u], scale, c);
+    }
+  }
+}
+
+// The stand-in over row slices (rows over 512 chunks), one chunk per lane:
+// the chunk's load, then the row's expert id, then the scaled store. y may
+// alias send (each chunk is read, then written, by one lane).
+template <int ACT>
+__global__ __launch_bounds__(kSliceChunks) void standin_slice_kernel(
+    const u32x4* send, const int32_t* __restrict__ src, const int32_t* __restrict__ idx, u32x4* y,
+    int n, int E, int cpr, int S, int first) {
+  declare_lds_reserve(cpr);
+  int r, c;
+  slice_of_block(S, first, r, c);
+  u32x4 v;
+  if (c < cpr) v = __builtin_nontemporal_load(send + (size_t)r * cpr + c);
+  const int sr = src[r];
+  const int e = static_cast<unsigned>(sr) < static_cast<unsigned>(n) ? idx[sr] : 0;
+  const float scale = 1.0f + static_cast<float>(e) / static_cast<float>(E);
+  if (c < cpr) {
+    float f[8];
+    unpack8<ACT>(to_uint4(v), f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = keep_f32(f[i] * scale);  // product rounded to fp32
+    __builtin_nontemporal_store(to_vec(pack8<ACT>(f)), y + (size_t)r * cpr + c);
   }
 }
 
@@ -194,7 +231,8 @@ __device__ __forceinline__ void combine_store(void* __restrict__ out, size_t chu
 //    the token's pos / w entries are read per slot (scalar loads when the
 //    row index is uniform). Used for short rows and rows of <= 256 chunks
 //    (H = 2048, k = 6: 83 us against 96 us for the batched shape).
-//  - U == 2 (one-row blocks, rows of more than 256 chunks): lanes 0..k-1 of
+//  - U == 2 (one-row blocks, rows of more than 256 chunks, except the large
+//    launches with k >= 5 that go out in slices, see combine_sliced): lanes 0..k-1 of
 //    each wave fetch the k pos / w entries in one vector load and broadcast
 //    them with readlane; each lane then issues the loads of two chunk
 //    positions before any math; with EXACT, k == KMAX is a compile-time
@@ -284,6 +322,48 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
       }
     }
   }
+}
+
+// The combine over row slices (rows over 256 chunks with k >= 5): a block
+// reads one 128-chunk slice of each of the token's k rows and writes that
+// slice of out, with the arithmetic of combine_kernel (fp32 FMAs in
+// ascending slot order, a bad pos read as row 0 with weight 0).
+template <int ACT, int KMAX, bool OUT_F32>
+__global__ __launch_bounds__(kSliceChunks) void combine_slice_kernel(
+    const u32x4* __restrict__ y, const int32_t* __restrict__ pos, const float* __restrict__ w,
+    void* __restrict__ out, int T, int k, int cpr, int S, int first) {
+  declare_lds_reserve(cpr);
+  int t, c;
+  slice_of_block(S, first, t, c);
+  size_t row[KMAX];
+  float wt[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      const int r = pos[(size_t)t * k + j];
+      const bool ok = static_cast<unsigned>(r) < static_cast<unsigned>(T * k);
+      row[j] = ok ? (size_t)r * cpr : 0;
+      wt[j] = ok ? w[(size_t)t * k + j] : 0.0f;
+    }
+  }
+  if (c >= cpr) return;
+  u32x4 v[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (j < k) v[j] = __builtin_nontemporal_load(y + row[j] + c);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      float f[8];
+      unpack8<ACT>(to_uint4(v[j]), f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt[j], f[i], acc[i]);
+    }
+  }
+  combine_store<ACT, OUT_F32>(out, (size_t)t * cpr + c, acc);
 }
 
 // Receiver fan-out of single-send rows: each single-send row q (token t =
@@ -392,18 +472,41 @@ int threads_per_row(int cpr) {
 // 0 to 64 KiB); each rule names the measured gain over no reservation.
 
 // Dispatch (plain and single-send), per launch shape (see launch_dispatch):
-//  - rows over 512 chunks, 128-thread blocks: 24 KiB at k <= 2, 32 KiB above
-//    (H = 7168: 5-8%);
-//  - 257-512 chunks, 256-thread blocks: 64 KiB at k >= 4 (H = 4096, k = 4:
-//    9%), else 48 KiB (H = 4096, k = 2: 71 vs 81 us);
+//  - row slices (dispatch_sliced), 128-thread blocks: 14 KiB for rows over
+//    512 chunks, 12 KiB for 257-512 chunks. The rate peaks sharply: at
+//    T = 65536, E = 256, k = 8, H = 7168, 1.53 ms at 14-15 KiB against
+//    1.59-1.73 ms at 8-13 KiB and 1.56-1.60 ms at 16-24 KiB; at T = 16384,
+//    E = 64, 12 KiB was 1-4% faster than 14 KiB, which serves both;
+//  - 257-512 chunks with k <= 4, 256-thread blocks: 64 KiB at k = 4
+//    (H = 4096: 9%), else 48 KiB (H = 4096, k = 2: 71 vs 81 us);
 //  - 129-256 chunks, 128-thread blocks: 24 KiB (measured with the shape);
 //  - at most 128 chunks, several rows per 256-thread block: 48 KiB.
-size_t dispatch_reserve(int k, int cpr) {
-  if (cpr > 512) return (k <= 2 ? 24 : 32) * kKiB;
+size_t dispatch_reserve(int k, int cpr, bool sliced) {
+  if (sliced) return (cpr > 512 ? 14 : 12) * kKiB;
+  if (cpr > 512) return 0;  // unsliced only in launches too small for a cap
   if (cpr > 256) return (k >= 4 ? 64 : 48) * kKiB;
   if (cpr > 128) return 24 * kKiB;
   return 48 * kKiB;
 }
+
+// Rows the dispatch cuts into slices (dispatch_slice_kernel): rows over 512
+// chunks, and rows of 257-512 chunks with k >= 5. Against one block per
+// token row (cold cache, T = 16384, E = 64 unless named): H = 7168, k = 2:
+// 113-118 against 123 us; k = 8: 368-380 against 392 us; T = 65536,
+// E = 256, k = 8: 1.53 against 1.61 ms; H = 8192, k = 2: 128-135 against
+// 143 us; H = 5120, k = 8: 265-272 against 278 us; H = 4096, k = 6: 160
+// against 181 us; k = 8: 211 against 235 us; H = 3072, k = 8: 160 against
+// 175 us. At H = 4096 with k = 2 and 4 slices were 1-2% slower (69.8
+// against 68.9 us, 112.6 against 110.7 us), at H = 2048, k = 8 equal.
+// The single-send dispatch writes fewer rows per token (one per distinct
+// rank) and is sliced only for rows over 512 chunks (T = 65536, E = 256,
+// k = 8, H = 7168: 1.42 against 1.48 ms); at 257-512 chunks slices were
+// mixed (H = 4096, k = 6: 125.5 against 123.7 us; k = 8: 160.8 against
+// 165.3 us; decode: 6.5 against 6.2 us).
+bool dispatch_sliced(int T, int k, int cpr) {
+  return (cpr > 512 || (cpr > 256 && k >= 5)) && enough_slices(T, slices_per_row(cpr));
+}
+bool ss_dispatch_sliced(int T, int cpr) { return cpr > 512 && enough_slices(T, slices_per_row(cpr)); }
 
 // The dispatch gives a block several rows whenever a row needs fewer than
 // kRowThreads lanes (rows of at most 128 chunks), so no lane idles while the
@@ -413,16 +516,24 @@ size_t dispatch_reserve(int k, int cpr) {
 // kernel with one row was 7% slower there).
 bool dispatch_multi_row(int cpr) { return threads_per_row(cpr) < kRowThreads; }
 
-// Blocks of a dispatch launch.
-long long dispatch_blocks(int T, int cpr) {
+// Blocks of a dispatch launch (all launches of a sliced one).
+long long dispatch_blocks(int T, int cpr, bool sliced) {
+  if (sliced) return (long long)T * slices_per_row(cpr);
   if (!dispatch_multi_row(cpr)) return T;
   const int per_blk = kRowThreads / threads_per_row(cpr);
   return (T + per_blk - 1) / per_blk;
 }
 
-// Stand-in: rows over 512 chunks, 24 KiB (H = 7168: 5-12%); shorter rows
-// were fastest with none.
-size_t standin_reserve(int cpr) { return cpr > 512 ? 24 * kKiB : 0; }
+// Stand-in: one-row blocks (rows of 64-512 chunks) were fastest with no
+// reservation. Rows over 512 chunks go out in slices, also with none (any
+// reservation from 4 to 32 KiB was slower); against one-row blocks with
+// 24 KiB (cold cache, T = 16384, E = 64 unless named): T = 65536, E = 256,
+// k = 8, H = 7168: 2.29 against 2.35 ms; H = 7168, k = 2: 149 against
+// 158 us; k = 8: 577 against 597 us; H = 8192, k = 2: 171 against 174 us.
+// Slices of 257-512-chunk rows were mixed (H = 4096, k = 8: 333 against
+// 339 us; k = 2: 86.5 against 84.6 us; H = 3072, k = 2: 69.5 against
+// 63.5 us).
+bool standin_sliced(int n, int cpr) { return cpr > 512 && enough_slices(n, slices_per_row(cpr)); }
 
 // Fan-out, two chunks per lane (rows over 256 chunks): 32 KiB at every k
 // measured (6-15%); rows of 256 chunks or fewer were fastest with none.
@@ -439,6 +550,19 @@ size_t combine_reserve(int k, int cpr) {
   if (k >= 3) return 48 * kKiB;
   return cpr > 512 ? 32 * kKiB : 0;
 }
+
+// Rows over 256 chunks with k >= 5 are combined in slices
+// (combine_slice_kernel), 24 KiB at k >= 7 and 16 KiB below. Against the
+// batched one-row shape (cold cache, T = 16384, E = 64 unless named):
+// T = 65536, E = 256, k = 8, H = 7168: 1.34 against 1.43-1.45 ms; H = 7168,
+// k = 8: 331 against 354 us; H = 4096, k = 8: 193 against 202 us; k = 6:
+// 151 against 160 us; H = 3072, k = 8: 149 against 160 us. With k <= 4
+// slices were slower or equal (H = 4096, k = 2: 70.3 against 66.7 us; k = 4:
+// 108.9 against 107.1 us; H = 7168, k = 4: 192.5 against 191.6 us).
+bool combine_sliced(int T, int k, int cpr) {
+  return cpr > kRowThreads && k >= 5 && enough_slices(T, slices_per_row(cpr));
+}
+size_t combine_slice_reserve(int k) { return (k >= 7 ? 24 : 16) * kKiB; }
 
 template <int ACT, bool OUT_F32, bool ONE>
 hipError_t launch_combine_k(const u32x4* y, const int32_t* pos, const float* w, void* out, int T,
@@ -473,6 +597,18 @@ hipError_t launch_combine_k(const u32x4* y, const int32_t* pos, const float* w, 
 template <int ACT, bool OUT_F32>
 hipError_t launch_combine_a(const u32x4* y, const int32_t* pos, const float* w, void* out, int T,
                             int k, int cpr, hipStream_t s) {
+  if (combine_sliced(T, k, cpr)) {
+    const int S = slices_per_row(cpr);
+    const size_t res = if_many_blocks(combine_slice_reserve(k), (long long)T * S);
+    slice_launches(T, S, [&](int first, unsigned blocks) {
+#define MOE_COMBINE_SLICE(KM) \
+  combine_slice_kernel<ACT, KM, OUT_F32><<<blocks, kSliceChunks, res, s>>>(y, pos, w, out, T, k, cpr, S, first)
+      if (k <= 8) MOE_COMBINE_SLICE(8);
+      else MOE_COMBINE_SLICE(16);
+#undef MOE_COMBINE_SLICE
+    });
+    return hipGetLastError();
+  }
   if (cpr >= kOneRowChunks) return launch_combine_k<ACT, OUT_F32, true>(y, pos, w, out, T, k, cpr, kRowThreads, T, s);
   const int tpt = threads_per_row(cpr);
   const int per_blk = kRowThreads / tpt;
@@ -489,10 +625,14 @@ hipError_t launch_combine_a(const u32x4* y, const int32_t* pos, const float* w, 
 //    block. Against 256-thread blocks with one chunk per lane (48 KiB):
 //    H = 2048, k = 2: 70 vs 90 us; H = 1536, k = 2: 56 vs 85 us; H = 1280,
 //    k = 4: 77 vs 98 us; H = 2048, k = 6: 86 us either way;
-//  - 257-512 chunks: 256-thread blocks, two chunks per lane;
-//  - longer rows (H = 7168): 128-thread blocks with ceil(cpr / 128) chunks
-//    per lane and serialized row loads (1.63 ms against 1.69-1.77 ms for
-//    256-thread shapes at full occupancy).
+//  - longer rows, and 257-512 chunks with k >= 5, in launches of at least
+//    kMinBlocksToCap slices: 128-chunk row slices, one block each (see
+//    dispatch_sliced). One 128-thread block per token row, ceil(cpr / 128)
+//    chunks per lane with serialized row loads, took 1.61-1.63 ms at
+//    H = 7168, k = 8 (256-thread blocks: 1.69-1.77 ms);
+//  - other rows over 256 chunks (k <= 4, the single-send dispatch at
+//    257-512 chunks, and small launches): 256-thread blocks, two chunks per
+//    lane, looping over rows beyond 512 chunks.
 
 hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T, int k, int H,
                            hipStream_t s) {
@@ -500,23 +640,22 @@ hipError_t launch_dispatch(const void* x, const int32_t* pos, void* send, int T,
   const int cpr = H / 8;
   const u32x4* xv = static_cast<const u32x4*>(x);
   u32x4* sv = static_cast<u32x4*>(send);
-  const size_t res = if_many_blocks(dispatch_reserve(k, cpr), dispatch_blocks(T, cpr));
-  if (dispatch_multi_row(cpr)) {
+  const bool sliced = dispatch_sliced(T, k, cpr);
+  const size_t res = if_many_blocks(dispatch_reserve(k, cpr, sliced), dispatch_blocks(T, cpr, sliced));
+  if (sliced) {
+    const int S = slices_per_row(cpr);
+    slice_launches(T, S, [&](int first, unsigned blocks) {
+      dispatch_slice_kernel<false><<<blocks, kSliceChunks, res, s>>>(xv, pos, sv, k, cpr, S, first, T * k);
+    });
+  } else if (dispatch_multi_row(cpr)) {
     const int tpt = threads_per_row(cpr);
     const int per_blk = kRowThreads / tpt;
     dispatch_kernel<kRowThreads, 1, false><<<(T + per_blk - 1) / per_blk, kRowThreads, res, s>>>(
         xv, pos, sv, T, k, cpr, tpt);
   } else if (cpr <= 256) {
-    dispatch_kernel<128, 2, true, false, false, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
-  } else if (cpr <= 512) {
-    dispatch_kernel<kRowThreads, 2, true><<<T, kRowThreads, res, s>>>(xv, pos, sv, T, k, cpr, 0);
+    dispatch_kernel<128, 2, true, false, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
   } else {
-    // ceil(cpr / 128) chunks per lane (a loop covers rows beyond 8 * 128)
-    const int u = (cpr + 127) / 128;
-    if (u <= 5) dispatch_kernel<128, 5, true, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
-    else if (u == 6) dispatch_kernel<128, 6, true, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
-    else if (u == 7) dispatch_kernel<128, 7, true, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
-    else dispatch_kernel<128, 8, true, true><<<T, 128, res, s>>>(xv, pos, sv, T, k, cpr, 0);
+    dispatch_kernel<kRowThreads, 2, true><<<T, kRowThreads, res, s>>>(xv, pos, sv, T, k, cpr, 0);
   }
   return hipGetLastError();
 }
@@ -527,19 +666,23 @@ hipError_t launch_single_send_dispatch(const void* x, const int32_t* ss_row, voi
   const int cpr = H / 8;
   const u32x4* xv = static_cast<const u32x4*>(x);
   u32x4* sv = static_cast<u32x4*>(send_ss);
-  const size_t res = if_many_blocks(dispatch_reserve(k, cpr), dispatch_blocks(T, cpr));
+  const bool sliced = ss_dispatch_sliced(T, cpr);
+  const size_t res = if_many_blocks(dispatch_reserve(k, cpr, sliced), dispatch_blocks(T, cpr, sliced));
   const int cap = ss_capacity;
-  if (dispatch_multi_row(cpr)) {
+  if (sliced) {
+    const int S = slices_per_row(cpr);
+    slice_launches(T, S, [&](int first, unsigned blocks) {
+      dispatch_slice_kernel<true><<<blocks, kSliceChunks, res, s>>>(xv, ss_row, sv, k, cpr, S, first, cap);
+    });
+  } else if (dispatch_multi_row(cpr)) {
     const int tpt = threads_per_row(cpr);
     const int per_blk = kRowThreads / tpt;
-    dispatch_kernel<kRowThreads, 1, false, false, true><<<(T + per_blk - 1) / per_blk, kRowThreads, res, s>>>(
+    dispatch_kernel<kRowThreads, 1, false, true><<<(T + per_blk - 1) / per_blk, kRowThreads, res, s>>>(
         xv, ss_row, sv, T, k, cpr, tpt, cap);
   } else if (cpr <= 256) {
-    dispatch_kernel<128, 2, true, false, true, true><<<T, 128, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
-  } else if (cpr <= 512) {
-    dispatch_kernel<kRowThreads, 2, true, false, true><<<T, kRowThreads, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
+    dispatch_kernel<128, 2, true, true, true><<<T, 128, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
   } else {
-    dispatch_kernel<128, 8, true, true, true><<<T, 128, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
+    dispatch_kernel<kRowThreads, 2, true, true><<<T, kRowThreads, res, s>>>(xv, ss_row, sv, T, k, cpr, 0, cap);
   }
   return hipGetLastError();
 }
@@ -575,15 +718,15 @@ hipError_t launch_standin(const void* send, const int32_t* src, const int32_t* i
   const int cpr = H / 8;
   const u32x4* in = static_cast<const u32x4*>(send);
   u32x4* out = static_cast<u32x4*>(y);
-  if (cpr >= kOneRowChunks) {
-    const size_t res = if_many_blocks(standin_reserve(cpr), n);
-    if (cpr > 512) {
-      if (act == 1) standin_kernel<1, true, 1><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
-      else standin_kernel<2, true, 1><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
-    } else {
-      if (act == 1) standin_kernel<1, true, 4><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
-      else standin_kernel<2, true, 4><<<n, kRowThreads, res, s>>>(in, src, idx, out, n, E, cpr, 0);
-    }
+  if (standin_sliced(n, cpr)) {
+    const int S = slices_per_row(cpr);
+    slice_launches(n, S, [&](int first, unsigned blocks) {
+      if (act == 1) standin_slice_kernel<1><<<blocks, kSliceChunks, 0, s>>>(in, src, idx, out, n, E, cpr, S, first);
+      else standin_slice_kernel<2><<<blocks, kSliceChunks, 0, s>>>(in, src, idx, out, n, E, cpr, S, first);
+    });
+  } else if (cpr >= kOneRowChunks) {
+    if (act == 1) standin_kernel<1, true, 4><<<n, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, 0);
+    else standin_kernel<2, true, 4><<<n, kRowThreads, 0, s>>>(in, src, idx, out, n, E, cpr, 0);
   } else {
     const int tpt = threads_per_row(cpr);
     const int per_blk = kRowThreads / tpt;

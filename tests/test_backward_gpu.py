@@ -185,6 +185,18 @@ def test_backward_row_widths(name, H, k):
     run_backward(synth.Workload(name, 300, 16, k, H, 4, synth.BF16, "zipf1.2", False), 6)
 
 
+# The dispatch backward in row slices (rows over 256 chunks, launches of at
+# least 4096 slices), at each of its LDS reservations (k = 2, 3, 4..6, 8)
+# and with ragged last slices (257, 375, 513 and 1537 chunks).
+SLICED = [("H2056_k3_T1400", 2056, 3, 1400), ("H3000_k8_T1400", 3000, 8, 1400),
+          ("H4104_k4_T1000", 4104, 4, 1000), ("H12296_k2_T400", 12296, 2, 400)]
+
+
+@pytest.mark.parametrize("name,H,k,T", SLICED, ids=[v[0] for v in SLICED])
+def test_backward_sliced_row_widths(name, H, k, T):
+    run_backward(synth.Workload(name, T, 16, k, H, 4, synth.BF16, "zipf1.2", False), 7)
+
+
 def test_backward_empty_batch_and_errors():
     w = synth.Workload("bwd_empty", 0, 8, 2, 128, 4, synth.F16, "none", False)
     say("[case] backward empty batch and argument errors")

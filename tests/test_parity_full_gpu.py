@@ -103,3 +103,44 @@ def test_max_rows():
     out_ref = oracle.combine(yref, np.arange(toks.shape[0] * k), ref_w.astype(np.float32), k, w.act_dtype)
     got = b.out.index_select(0, torch.from_numpy(toks).to(b.out.device)).float().cpu().numpy().astype(np.float64)
     assert (np.abs(got - out_ref) <= 1e-3 + 4e-3 * np.abs(out_ref)).all(), "combine of sampled tokens"
+
+
+def test_wide_rows_over_several_dispatch_launches():
+    """Rows of 2048 chunks (H = 16384) go out in 16 slices of 128 chunks, one
+    block each, and one launch takes at most 2^20 such blocks: T = 65600
+    tokens make 1,049,600 of them, so the dispatch and the single-send
+    dispatch each run as two launches (65536 tokens, then 64). The index
+    outputs are compared whole with the oracle; every send row, and every
+    single-send row, is checked against its token's row on the GPU. The
+    activations are drawn on the GPU (seeded): only these identities use
+    them."""
+    from combine_router_topk_amd import binding as B
+    from combine_router_topk_amd import path as P
+    T, E, k, H, R = 65600, 16, 2, 16384, 4
+    w = synth.Workload(f"wide_T{T}_E{E}_k{k}_H{H}", T, E, k, H, R, synth.BF16, "zipf1.2", False)
+    say(f"[case] {w.name}: sliced dispatch over two launches")
+    logits = synth.make_logits(w, 0)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
+    p = B.make_problem(T, E, k, H, R, B.MOE_BF16)
+    b = P.allocate(p, torch.from_numpy(logits), x)
+    del x
+    b.send.fill_(7.0)
+    P.route_assign_layout(b)
+    P.dispatch(b)
+    ss = P.allocate_single_send(b)
+    P.layout_single_send(b, ss)
+    ss.send_ss.fill_(7.0)
+    P.single_send_dispatch(b, ss)
+    torch.cuda.synchronize()
+    ref = oracle.route_and_layout(T, E, k, R, logits, None)
+    check_meta(b, ref, T, k)
+    dispatch_identity_all_rows(b, k)
+    n_ss = int(ss.ss_rank_offsets[R])
+    assert n_ss == int(ref["dedup"].sum())
+    tok = ss.ss_token[:n_ss].long()
+    step = 1 << 15
+    for r0 in range(0, n_ss, step):
+        r1 = min(n_ss, r0 + step)
+        assert torch.equal(ss.send_ss[r0:r1].view(torch.int16),
+                           b.x.index_select(0, tok[r0:r1]).view(torch.int16)), r0

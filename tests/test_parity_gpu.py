@@ -89,11 +89,12 @@ EDGE = [
 ]
 
 
-# Row widths at every launch-shape boundary of the row kernels (16-byte
+# Row widths at every launch-shape boundary of the one-row kernels (16-byte
 # chunks per row): 257 and 375 (two chunks per lane, the second ragged),
-# 513, 768 and 1024 (the 128-thread dispatch with 5, 6 and 8 chunks per
-# lane), 1537 (rows past 1024 chunks: the dispatch loops); k from 3 to 8
-# covers the combine's compile-time-k instances.
+# 513, 768, 1024 and 1537 (rows past 512 chunks: the 256-thread dispatch
+# loops); k from 3 to 8 covers the combine's compile-time-k instances. At
+# T = 300 every launch here has fewer than 4096 row slices, so none is
+# sliced.
 WIDTHS = [("H1024_k4", 1024, 4), ("H1032_k2", 1032, 2), ("H2048_k6", 2048, 6),
           ("H2056_k3", 2056, 3), ("H3000_k5", 3000, 5), ("H4104_k4", 4104, 4),
           ("H6144_k6", 6144, 6), ("H8192_k8", 8192, 8), ("H12296_k7", 12296, 7)]
@@ -102,6 +103,20 @@ WIDTHS = [("H1024_k4", 1024, 4), ("H1032_k2", 1032, 2), ("H2048_k6", 2048, 6),
 @pytest.mark.parametrize("name,H,k", WIDTHS, ids=[v[0] for v in WIDTHS])
 def test_row_widths(name, H, k):
     run_and_check(synth.Workload(name, 300, 16, k, H, 4, synth.BF16, "zipf1.2", False), 6)
+
+
+# The row-slice kernels (128-chunk slices, one block each, in launches of at
+# least 4096 slices): the dispatch for rows over 512 chunks or k >= 5, the
+# stand-in over 512 chunks, the combine with k >= 5, with a ragged last
+# slice at 375, 513 and 1537 chunks (119, 1 and 1 chunks), in both
+# activation formats.
+SLICED = [("H3000_k5_T1400", 3000, 5, 1400, synth.BF16), ("H4104_k6_T1000_f16", 4104, 6, 1000, synth.F16),
+          ("H6144_k8_T700", 6144, 8, 700, synth.BF16), ("H12296_k7_T400", 12296, 7, 400, synth.BF16)]
+
+
+@pytest.mark.parametrize("name,H,k,T,act", SLICED, ids=[v[0] for v in SLICED])
+def test_sliced_row_widths(name, H, k, T, act):
+    run_and_check(synth.Workload(name, T, 16, k, H, 4, act, "zipf1.2", False), 7)
 
 
 @pytest.mark.parametrize("name,T,E,k,R,H", EDGE, ids=[e[0] for e in EDGE])

@@ -142,6 +142,21 @@ def test_single_send_row_widths(name, H, k):
     check_single_send(w, b, ss, ex, ref)
 
 
+# The single-send dispatch in row slices (rows over 512 chunks, launches of
+# at least 4096 slices), with ragged last slices (513 and 1537 chunks).
+SLICED = [("H4104_k4_T1000", 4104, 4, 1000), ("H12296_k7_T400", 12296, 7, 400)]
+
+
+@pytest.mark.parametrize("name,H,k,T", SLICED, ids=[v[0] for v in SLICED])
+def test_single_send_sliced_row_widths(name, H, k, T):
+    w = synth.Workload(name, T, 16, k, H, 4, synth.BF16, "zipf1.2", False)
+    say(f"[case] single-send sliced row width {name}")
+    logits, x = synth.make_logits(w, 7), synth.make_x(w, 7)
+    ref = oracle.route_and_layout(w.T, w.E, w.k, w.R, logits)
+    b, ss, ex = run_single_send(w, logits, x, None)
+    check_single_send(w, b, ss, ex, ref)
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_single_send_random_replicas_id_order(seed):
     rng = np.random.default_rng(300 + seed)
