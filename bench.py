@@ -79,6 +79,19 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def row_kernel_names(T: int, k: int, H: int):
+    """Names of the dispatch and combine kernels that launches of this shape
+    run, for the roofline entries. They follow the launch rules of the
+    library's row kernels: 128-chunk row slices, in launches of at least
+    4096 slices, for dispatch rows over 512 chunks or over 256 chunks with
+    k >= 5, and for combine rows over 256 chunks with k >= 5."""
+    cpr = H // 8
+    many = T * -(-cpr // 128) >= 4096
+    d = "dispatch_slice_kernel" if (cpr > 512 or (cpr > 256 and k >= 5)) and many else "dispatch_kernel"
+    c = "combine_slice_kernel" if cpr > 256 and k >= 5 and many else "combine_kernel"
+    return d, c
+
+
 def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 PMC counters, if the
     counters were taken on the current kernel source for this workload."""
@@ -610,7 +623,8 @@ def workloads_leg(P, B, synth, np, torch, dev, flush, ev, seed, steps, skip) -> 
         plan_ms, d_ms, c_ms = avg(0), avg(2), avg(4)
         half = (1 + w.k) * w.T * w.H * 2
         dc = 2 * half
-        dom, dom_ms = ("dispatch_kernel", d_ms) if d_ms >= c_ms else ("combine_kernel", c_ms)
+        dname, cname = row_kernel_names(w.T, w.k, w.H)
+        dom, dom_ms = (dname, d_ms) if d_ms >= c_ms else (cname, c_ms)
         gbps = dc / ((d_ms + c_ms) / 1e3) / 1e9
         out[w.name] = {
             "stage_us": {"plan": round(plan_ms * 1e3, 2), "dispatch": round(d_ms * 1e3, 2),
@@ -743,7 +757,8 @@ def main():
     dc_bytes = 2 * half
     dc_s = (disp_ms + comb_ms) / 1e3
     value = dc_bytes / dc_s / 1e9
-    dom, dom_ms = ("dispatch_kernel", disp_ms) if disp_ms >= comb_ms else ("combine_kernel", comb_ms)
+    dname, cname = row_kernel_names(w.T, w.k, w.H)
+    dom, dom_ms = (dname, disp_ms) if disp_ms >= comb_ms else (cname, comb_ms)
     achieved = half / (dom_ms / 1e3) / 1e9
     traffic = traffic_from_profiles(dom, w.name)
 

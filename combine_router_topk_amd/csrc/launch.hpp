@@ -33,9 +33,10 @@ inline size_t if_many_blocks(size_t res, long long blocks) {
 // Sliced launches (see slice_of_block) take at most kMaxSliceBlocks blocks
 // each, whole rows, which keeps every grid far below the 2^32 work-items a
 // launch can address; every workload here fits one launch (T = 65536 at
-// H = 7168 is 458,752 blocks for the dispatch). slice_launches calls
-// launch(first_row, blocks) for each launch of `rows` rows of S slices.
-constexpr long long kMaxSliceBlocks = 1 << 20;
+// H = 7168: 458,752 blocks for the dispatch, 3,670,016 for the stand-in's
+// T k rows). slice_launches calls launch(first_row, blocks) for each launch
+// of `rows` rows of S slices.
+constexpr long long kMaxSliceBlocks = 1 << 22;
 // A kernel slices its rows only when that gives at least kMinBlocksToCap
 // blocks: smaller launches are latency-bound, and there one-row blocks,
 // which issue their index loads alongside the row loads, finish sooner

@@ -107,24 +107,29 @@ def test_max_rows():
 
 def test_wide_rows_over_several_dispatch_launches():
     """Rows of 2048 chunks (H = 16384) go out in 16 slices of 128 chunks, one
-    block each, and one launch takes at most 2^20 such blocks: T = 65600
-    tokens make 1,049,600 of them, so the dispatch and the single-send
-    dispatch each run as two launches (65536 tokens, then 64). The index
+    block each, and one launch takes at most 2^22 such blocks: T = 262200
+    tokens make 4,195,200 of them, so the dispatch and the single-send
+    dispatch each run as two launches (262144 tokens, then 56). The index
     outputs are compared whole with the oracle; every send row, and every
     single-send row, is checked against its token's row on the GPU. The
-    activations are drawn on the GPU (seeded): only these identities use
-    them."""
+    activations (8.6 GB) are drawn on the GPU (seeded): only these
+    identities use them."""
     from combine_router_topk_amd import binding as B
     from combine_router_topk_amd import path as P
-    T, E, k, H, R = 65600, 16, 2, 16384, 4
+    T, E, k, H, R = 262200, 8, 1, 16384, 4
     w = synth.Workload(f"wide_T{T}_E{E}_k{k}_H{H}", T, E, k, H, R, synth.BF16, "zipf1.2", False)
     say(f"[case] {w.name}: sliced dispatch over two launches")
     logits = synth.make_logits(w, 0)
     g = torch.Generator(device="cuda").manual_seed(5)
-    x = torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
+    x = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    for t0 in range(0, T, 1 << 15):  # drawn in pieces to bound the fp32 temporaries
+        t1 = min(T, t0 + (1 << 15))
+        x[t0:t1] = torch.randn(t1 - t0, H, generator=g, device="cuda").to(torch.bfloat16)
     p = B.make_problem(T, E, k, H, R, B.MOE_BF16)
     b = P.allocate(p, torch.from_numpy(logits), x)
     del x
+    b.y = b.out = None  # not used here
+    torch.cuda.empty_cache()
     b.send.fill_(7.0)
     P.route_assign_layout(b)
     P.dispatch(b)
