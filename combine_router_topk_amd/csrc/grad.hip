@@ -194,6 +194,33 @@ __global__ __launch_bounds__(kGradThreads) void combine_backward_kernel(
   }
 }
 
+// dy alone over row slices (see combine_backward_split): a block loads one
+// 128-chunk slice of dout and writes w[t,j] * dout, rounded as in
+// combine_backward_kernel, to the same slice of each valid slot's dy row.
+template <int ACT>
+__global__ __launch_bounds__(kSliceChunks) void combine_backward_dy_slice_kernel(
+    const u32x4* __restrict__ dout, const int32_t* __restrict__ pos, const float* __restrict__ w,
+    u32x4* dy, int T, int k, int cpr, int S, int first) {
+  declare_lds_reserve(cpr);
+  int t, c;
+  slice_of_block(S, first, t, c);
+  const int n_rows = T * k;
+  u32x4 gv;
+  if (c < cpr) gv = __builtin_nontemporal_load(dout + (size_t)t * cpr + c);
+  for (int j = 0; j < k; ++j) {
+    const int r = pos[(size_t)t * k + j];
+    if (static_cast<unsigned>(r) >= static_cast<unsigned>(n_rows)) continue;
+    const float wj = w[(size_t)t * k + j];
+    if (c < cpr) {
+      float gf[8], p[8];
+      unpack8<ACT>(as_uint4(gv), gf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = keep_f32(wj * gf[i]);  // fp32 product, then one rounding
+      __builtin_nontemporal_store(as_vec(pack8<ACT>(p)), dy + (size_t)r * cpr + c);
+    }
+  }
+}
+
 template <int ACT, bool OUT_F32>
 __device__ __forceinline__ void grad_store(void* __restrict__ out, size_t chunk, const float (&acc)[8]) {
   if constexpr (OUT_F32) {
@@ -335,6 +362,26 @@ hipError_t launch_cb(const u32x4* dout, const u32x4* y, const int32_t* pos, cons
   return hipGetLastError();
 }
 
+// With wide rows and many slots the combine backward runs as two launches:
+// dw alone (combine_backward_kernel without dy: dout and the k y rows read,
+// nothing but dw written), then dy alone in row slices, dispatch-shaped
+// (reservations as the dispatch's slices: 14 KiB over 512 chunks, else
+// 12 KiB). That reads dout twice, (2k + 2) H b per token instead of
+// (2k + 1) H b, but each half runs at its own kernel's rate: at T = 65536,
+// E = 256, k = 8, H = 7168 the fused kernel took 3.11 ms, dw alone 1.26 ms
+// and dy alone 1.75 ms in one-row blocks; split, with dy in slices, it
+// takes 2.80 ms. Split only in large launches (at least kMinBlocksToCap
+// slices) with k >= 5 and rows over 256 chunks whose k dy rows hold at
+// least 64 KiB (k * cpr >= 4096), where it measured faster (cold cache,
+// T = 16384, E = 64): H = 7168, k = 5: 454 against 485 us; k = 6: 534
+// against 576 us; H = 4096, k = 8: 415 against 433 us. Below that it was
+// slower: H = 4096, k = 5: 270 against 265 us; k = 6: 321 against 316 us;
+// H = 3072, k = 8: 329 against 319 us; and at train top-2 the one-row
+// halves took 75.7 + 64.8 us against 127.2 us fused.
+bool combine_backward_split(int T, int k, int cpr) {
+  return cpr > 256 && k >= 5 && k * cpr >= 4096 && enough_slices(T, slices_per_row(cpr));
+}
+
 template <int ACT>
 hipError_t launch_cb_k(const u32x4* dout, const u32x4* y, const int32_t* pos, const float* w,
                        u32x4* dy, float* dw, int T, int k, int cpr, hipStream_t s) {
@@ -409,6 +456,23 @@ hipError_t launch_combine_backward(const void* dout, const void* y, const int32_
   const u32x4* g = static_cast<const u32x4*>(dout);
   const u32x4* yv = static_cast<const u32x4*>(y);
   u32x4* dyv = static_cast<u32x4*>(dy);
+  if (dy != nullptr && combine_backward_split(T, k, cpr)) {
+    // dw first: it reads y, which dy may alias
+    if (dw != nullptr) {
+      const hipError_t e = act == 1 ? launch_cb_k<1>(g, yv, pos, w, nullptr, dw, T, k, cpr, s)
+                                    : launch_cb_k<2>(g, yv, pos, w, nullptr, dw, T, k, cpr, s);
+      if (e != hipSuccess) return e;
+    }
+    const int S = slices_per_row(cpr);
+    const size_t res = if_many_blocks((cpr > 512 ? 14 : 12) * kKiB, (long long)T * S);
+    slice_launches(T, S, [&](int first, unsigned blocks) {
+      if (act == 1)
+        combine_backward_dy_slice_kernel<1><<<blocks, kSliceChunks, res, s>>>(g, pos, w, dyv, T, k, cpr, S, first);
+      else
+        combine_backward_dy_slice_kernel<2><<<blocks, kSliceChunks, res, s>>>(g, pos, w, dyv, T, k, cpr, S, first);
+    });
+    return hipGetLastError();
+  }
   return act == 1 ? launch_cb_k<1>(g, yv, pos, w, dyv, dw, T, k, cpr, s)
                   : launch_cb_k<2>(g, yv, pos, w, dyv, dw, T, k, cpr, s);
 }

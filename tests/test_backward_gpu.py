@@ -142,13 +142,22 @@ def test_backward_fp32_dx(w):
     run_backward(w, 1, flags=B.MOE_FLAG_OUT_F32)
 
 
+# The second workload of each pair is split into a dw launch and a sliced dy
+# launch (rows over 256 chunks, k >= 5, at least 4096 slices): dy alone
+# then runs only the slices, and dy in place of y needs dw's reads of y to
+# come first.
+SPLIT = synth.scaled(synth.LARGE, T=777, H=7168)
+
+
 @pytest.mark.parametrize("outputs", [("dy",), ("dw",)])
-def test_backward_single_output(outputs):
-    run_backward(synth.scaled(synth.TRAIN_TOP6, T=700, H=520), 2, outputs=outputs)
+@pytest.mark.parametrize("w", [synth.scaled(synth.TRAIN_TOP6, T=700, H=520), SPLIT], ids=lambda w: w.name)
+def test_backward_single_output(w, outputs):
+    run_backward(w, 2, outputs=outputs)
 
 
-def test_backward_dy_in_place_of_y():
-    run_backward(synth.scaled(synth.TRAIN_TOP2, T=1000, H=256), 3, alias=True)
+@pytest.mark.parametrize("w", [synth.scaled(synth.TRAIN_TOP2, T=1000, H=256), SPLIT], ids=lambda w: w.name)
+def test_backward_dy_in_place_of_y(w):
+    run_backward(w, 3, alias=True)
 
 
 def test_backward_chain_dsend_is_dy():
@@ -187,9 +196,11 @@ def test_backward_row_widths(name, H, k):
 
 # The dispatch backward in row slices (rows over 256 chunks, launches of at
 # least 4096 slices), at each of its LDS reservations (k = 2, 3, 4..6, 8)
-# and with ragged last slices (257, 375, 513 and 1537 chunks).
+# and with ragged last slices (257, 375, 513 and 1537 chunks); with k >= 5
+# the combine backward there is split into dw and sliced dy.
 SLICED = [("H2056_k3_T1400", 2056, 3, 1400), ("H3000_k8_T1400", 3000, 8, 1400),
-          ("H4104_k4_T1000", 4104, 4, 1000), ("H12296_k2_T400", 12296, 2, 400)]
+          ("H4104_k4_T1000", 4104, 4, 1000), ("H12296_k2_T400", 12296, 2, 400),
+          ("H12296_k6_T400", 12296, 6, 400)]
 
 
 @pytest.mark.parametrize("name,H,k,T", SLICED, ids=[v[0] for v in SLICED])
