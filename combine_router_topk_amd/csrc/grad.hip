@@ -370,16 +370,18 @@ hipError_t launch_cb(const u32x4* dout, const u32x4* y, const int32_t* pos, cons
 // (2k + 1) H b, but each half runs at its own kernel's rate: at T = 65536,
 // E = 256, k = 8, H = 7168 the fused kernel took 3.11 ms, dw alone 1.26 ms
 // and dy alone 1.75 ms in one-row blocks; split, with dy in slices, it
-// takes 2.80 ms. Split only in large launches (at least kMinBlocksToCap
-// slices) with k >= 5 and rows over 256 chunks whose k dy rows hold at
-// least 64 KiB (k * cpr >= 4096), where it measured faster (cold cache,
+// takes 2.80 ms. Split only in launches of at least 8192 slices with
+// k >= 5 and rows over 256 chunks whose k dy rows hold at least 64 KiB
+// (k * cpr >= 4096), where it measured faster (cold cache,
 // T = 16384, E = 64): H = 7168, k = 5: 454 against 485 us; k = 6: 534
 // against 576 us; H = 4096, k = 8: 415 against 433 us. Below that it was
 // slower: H = 4096, k = 5: 270 against 265 us; k = 6: 321 against 316 us;
 // H = 3072, k = 8: 329 against 319 us; and at train top-2 the one-row
 // halves took 75.7 + 64.8 us against 127.2 us fused.
+// Smaller launches stay fused (H = 4096, k = 8, T = 1100: 37.3 against
+// 35.6 us fused; T = 2048: 59.1 against 60.1 us).
 bool combine_backward_split(int T, int k, int cpr) {
-  return cpr > 256 && k >= 5 && k * cpr >= 4096 && enough_slices(T, slices_per_row(cpr));
+  return cpr > 256 && k >= 5 && k * cpr >= 4096 && enough_slices(T, slices_per_row(cpr), 8192);
 }
 
 template <int ACT>
@@ -392,8 +394,8 @@ hipError_t launch_cb_k(const u32x4* dout, const u32x4* y, const int32_t* pos, co
 }
 
 // The dispatch backward cuts rows over 256 chunks into slices
-// (dispatch_backward_slice_kernel) in launches of at least kMinBlocksToCap
-// slices; shorter rows, and smaller launches, keep one-row blocks, fastest
+// (dispatch_backward_slice_kernel) in launches of at least 12288 slices
+// (below); shorter rows, and smaller launches, keep one-row blocks, fastest
 // with no LDS reservation. The slices' reservation grows
 // with k, which sets the row loads in flight per block: none at k <= 2,
 // 4 KiB at k = 3, 16 KiB at k = 4..6, 24 KiB above. Against one-row blocks
@@ -403,8 +405,12 @@ hipError_t launch_cb_k(const u32x4* dout, const u32x4* y, const int32_t* pos, co
 // H = 4096, k = 2: 67.4 against 69.2 us; k = 3: 84.1 against 92.5 us;
 // k = 4: 108 against 111 us; k = 6: 152 against 165 us; H = 3072, k = 2:
 // 50.8 against 57.1 us; k = 8: 152 against 166 us.
+// Launches of at least 12288 slices: at k = 8 slices were slower in smaller
+// ones (H = 7168, T = 1024: 27.6 against 26.7 us; H = 4096, T = 2048: 30.7
+// against 29.9 us) and faster from there (H = 7168, T = 2048: 48.6 against
+// 52.7 us; H = 4096, T = 4096: 54.5 against 56.1 us).
 bool dispatch_backward_sliced(int T, int cpr) {
-  return cpr > 256 && enough_slices(T, slices_per_row(cpr));
+  return cpr > 256 && enough_slices(T, slices_per_row(cpr), 12288);
 }
 size_t dispatch_backward_slice_reserve(int k) {
   if (k <= 2) return 0;

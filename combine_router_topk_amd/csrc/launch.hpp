@@ -37,12 +37,15 @@ inline size_t if_many_blocks(size_t res, long long blocks) {
 // T k rows). slice_launches calls launch(first_row, blocks) for each launch
 // of `rows` rows of S slices.
 constexpr long long kMaxSliceBlocks = 1 << 22;
-// A kernel slices its rows only when that gives at least kMinBlocksToCap
-// blocks: smaller launches are latency-bound, and there one-row blocks,
-// which issue their index loads alongside the row loads, finish sooner
-// (decode, T = 256, k = 8, H = 4096: combine 9.9 us in 1024 slices against
-// 6.9 us in 256 one-row blocks; dispatch backward 10.4 against 9.4 us).
-inline bool enough_slices(long long rows, int slices) { return rows * slices >= kMinBlocksToCap; }
+// A kernel slices its rows only in launches of at least `min_slices`
+// slices (kMinBlocksToCap unless its launcher names more): smaller launches
+// are latency-bound, and there one-row blocks, which issue their index loads
+// alongside the row loads, finish sooner (decode, T = 256, k = 8,
+// H = 4096: combine 9.9 us in 1024 slices against 6.9 us in 256 one-row
+// blocks; dispatch backward 10.4 against 9.4 us).
+inline bool enough_slices(long long rows, int slices, long long min_slices = kMinBlocksToCap) {
+  return rows * slices >= min_slices;
+}
 template <typename F>
 inline void slice_launches(int rows, int S, F&& launch) {
   const long long per_ll = kMaxSliceBlocks / S;

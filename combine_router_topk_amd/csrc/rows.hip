@@ -503,8 +503,14 @@ size_t dispatch_reserve(int k, int cpr, bool sliced) {
 // k = 8, H = 7168: 1.42 against 1.48 ms); at 257-512 chunks slices were
 // mixed (H = 4096, k = 6: 125.5 against 123.7 us; k = 8: 160.8 against
 // 165.3 us; decode: 6.5 against 6.2 us).
+// Rows of 257-512 chunks need launches of 16384 slices: at H = 4096, k = 8
+// slices were slower at T = 1100 and 2048 (16.9 against 16.0 us, 29.9
+// against 29.0 us) and faster from T = 4096 (55.6 against 59.8 us); rows
+// over 512 chunks were faster from the smallest launch sliced (H = 7168,
+// k = 8, T = 600: 15.1 against 17.8 us).
 bool dispatch_sliced(int T, int k, int cpr) {
-  return (cpr > 512 || (cpr > 256 && k >= 5)) && enough_slices(T, slices_per_row(cpr));
+  if (cpr > 512) return enough_slices(T, slices_per_row(cpr));
+  return cpr > 256 && k >= 5 && enough_slices(T, slices_per_row(cpr), 16384);
 }
 bool ss_dispatch_sliced(int T, int cpr) { return cpr > 512 && enough_slices(T, slices_per_row(cpr)); }
 
@@ -559,8 +565,12 @@ size_t combine_reserve(int k, int cpr) {
 // 151 against 160 us; H = 3072, k = 8: 149 against 160 us. With k <= 4
 // slices were slower or equal (H = 4096, k = 2: 70.3 against 66.7 us; k = 4:
 // 108.9 against 107.1 us; H = 7168, k = 4: 192.5 against 191.6 us).
+// Only in launches of at least 12288 slices: below, the one-row shape was
+// faster (k = 8, H = 7168, T = 1024: 25.7 against 27.6 us in slices;
+// H = 4096, T = 2048: 28.3 against 30.5 us); above, slices (H = 7168,
+// T = 2048: 48.4 against 49.5 us; H = 4096, T = 4096: 54.0 against 55.6 us).
 bool combine_sliced(int T, int k, int cpr) {
-  return cpr > kRowThreads && k >= 5 && enough_slices(T, slices_per_row(cpr));
+  return cpr > kRowThreads && k >= 5 && enough_slices(T, slices_per_row(cpr), 12288);
 }
 size_t combine_slice_reserve(int k) { return (k >= 7 ? 24 : 16) * kKiB; }
 

@@ -143,10 +143,10 @@ def test_backward_fp32_dx(w):
 
 
 # The second workload of each pair is split into a dw launch and a sliced dy
-# launch (rows over 256 chunks, k >= 5, at least 4096 slices): dy alone
-# then runs only the slices, and dy in place of y needs dw's reads of y to
-# come first.
-SPLIT = synth.scaled(synth.LARGE, T=777, H=7168)
+# launch (rows over 256 chunks, k >= 5, k dy rows of at least 64 KiB, at
+# least 8192 slices): dy alone then runs only the slices, and dy in place of
+# y needs dw's reads of y to come first.
+SPLIT = synth.scaled(synth.LARGE, T=1200, H=7168)
 
 
 @pytest.mark.parametrize("outputs", [("dy",), ("dw",)])
@@ -195,12 +195,12 @@ def test_backward_row_widths(name, H, k):
 
 
 # The dispatch backward in row slices (rows over 256 chunks, launches of at
-# least 4096 slices), at each of its LDS reservations (k = 2, 3, 4..6, 8)
-# and with ragged last slices (257, 375, 513 and 1537 chunks); with k >= 5
-# the combine backward there is split into dw and sliced dy.
-SLICED = [("H2056_k3_T1400", 2056, 3, 1400), ("H3000_k8_T1400", 3000, 8, 1400),
-          ("H4104_k4_T1000", 4104, 4, 1000), ("H12296_k2_T400", 12296, 2, 400),
-          ("H12296_k6_T400", 12296, 6, 400)]
+# least 12288 slices), at each of its LDS reservations (k = 2, 3, 4..6, 8)
+# and with ragged last slices (257, 375, 513 and 1537 chunks); at 1537
+# chunks with k = 6 the combine backward is split into dw and sliced dy.
+SLICED = [("H2056_k3_T4200", 2056, 3, 4200), ("H3000_k8_T4200", 3000, 8, 4200),
+          ("H4104_k4_T2500", 4104, 4, 2500), ("H12296_k2_T1000", 12296, 2, 1000),
+          ("H12296_k6_T1000", 12296, 6, 1000)]
 
 
 @pytest.mark.parametrize("name,H,k,T", SLICED, ids=[v[0] for v in SLICED])

@@ -105,13 +105,14 @@ def test_row_widths(name, H, k):
     run_and_check(synth.Workload(name, 300, 16, k, H, 4, synth.BF16, "zipf1.2", False), 6)
 
 
-# The row-slice kernels (128-chunk slices, one block each, in launches of at
-# least 4096 slices): the dispatch for rows over 512 chunks or k >= 5, the
-# stand-in over 512 chunks, the combine with k >= 5, with a ragged last
-# slice at 375, 513 and 1537 chunks (119, 1 and 1 chunks), in both
-# activation formats.
-SLICED = [("H3000_k5_T1400", 3000, 5, 1400, synth.BF16), ("H4104_k6_T1000_f16", 4104, 6, 1000, synth.F16),
-          ("H6144_k8_T700", 6144, 8, 700, synth.BF16), ("H12296_k7_T400", 12296, 7, 400, synth.BF16)]
+# The row-slice kernels (128-chunk slices, one block each): the dispatch for
+# rows over 512 chunks (launches of at least 4096 slices) or of 257-512
+# chunks with k >= 5 (16384 slices), the stand-in over 512 chunks (4096),
+# the combine with k >= 5 (12288), each case past every threshold it
+# meets, with a ragged last slice at 375, 513 and 1537 chunks (119, 1 and
+# 1 chunks), in both activation formats.
+SLICED = [("H3000_k5_T5500", 3000, 5, 5500, synth.BF16), ("H4104_k6_T2500_f16", 4104, 6, 2500, synth.F16),
+          ("H6144_k8_T2100", 6144, 8, 2100, synth.BF16), ("H12296_k7_T1000", 12296, 7, 1000, synth.BF16)]
 
 
 @pytest.mark.parametrize("name,H,k,T,act", SLICED, ids=[v[0] for v in SLICED])
