@@ -82,13 +82,15 @@ def kernel_source_digest() -> str:
 def row_kernel_names(T: int, k: int, H: int):
     """Names of the dispatch and combine kernels that launches of this shape
     run, for the roofline entries. They follow the launch rules of the
-    library's row kernels: 128-chunk row slices, in launches of at least
-    4096 slices, for dispatch rows over 512 chunks or over 256 chunks with
-    k >= 5, and for combine rows over 256 chunks with k >= 5."""
+    library's row kernels: 128-chunk row slices for dispatch rows over 512
+    chunks in launches of at least 4096 slices, or of 257-512 chunks with
+    k >= 5 in launches of at least 16384, and for combine rows over 256
+    chunks with k >= 5 in launches of at least 12288."""
     cpr = H // 8
-    many = T * -(-cpr // 128) >= 4096
-    d = "dispatch_slice_kernel" if (cpr > 512 or (cpr > 256 and k >= 5)) and many else "dispatch_kernel"
-    c = "combine_slice_kernel" if cpr > 256 and k >= 5 and many else "combine_kernel"
+    slices = T * -(-cpr // 128)
+    sliced_d = (cpr > 512 and slices >= 4096) or (cpr > 256 and k >= 5 and slices >= 16384)
+    d = "dispatch_slice_kernel" if sliced_d else "dispatch_kernel"
+    c = "combine_slice_kernel" if cpr > 256 and k >= 5 and slices >= 12288 else "combine_kernel"
     return d, c
 
 
