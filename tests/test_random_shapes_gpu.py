@@ -12,6 +12,8 @@ tests: bit-exact indices, counts, offsets and rows, gate weights within rtol
 outputs within their accumulation bound)."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 
@@ -28,7 +30,11 @@ from test_stats_gpu import run_stats
 
 import oracle
 
-N_CASES = 64
+# The committed sweep: 64 shapes from one seed. MOE_RANDOM_SEED and
+# MOE_RANDOM_CASES draw another sweep of any length through the same checks.
+DEFAULT_SEED, DEFAULT_CASES = 20_261_203, 64
+SWEEP_SEED = int(os.environ.get("MOE_RANDOM_SEED", DEFAULT_SEED))
+N_CASES = int(os.environ.get("MOE_RANDOM_CASES", DEFAULT_CASES))
 ELEMENT_BUDGET = 12_000_000   # T*k*H: the oracle's rows stay at a few seconds
 LARGE_BUDGET = 24_000_000     # one case in four: enough rows for the occupancy-capped launches
 CHUNK_BANDS = [(1, 64), (65, 128), (129, 256), (257, 512), (513, 1100)]
@@ -55,12 +61,13 @@ def draw_problem(i: int, rng: np.random.Generator) -> dict:
                 ties=bool(rng.random() < 0.3), seed=int(rng.integers(1 << 30)))
 
 
-def problems(n: int) -> list[dict]:
-    rng = np.random.default_rng(20_261_203)
+def problems(n: int, seed: int) -> list[dict]:
+    rng = np.random.default_rng(seed)
     return [draw_problem(i, rng) for i in range(n)]
 
 
-PROBLEMS = problems(N_CASES)
+DEFAULT_PROBLEMS = problems(DEFAULT_CASES, DEFAULT_SEED)
+PROBLEMS = problems(N_CASES, SWEEP_SEED)
 
 
 def case_id(c: dict) -> str:
@@ -81,14 +88,15 @@ def inputs(c: dict):
 
 
 def test_problem_draws_cover_every_band():
-    """The seeded draws reach every row-width band, both formats, replica
+    """The committed draws reach every row-width band, both formats, replica
     tables, E past 128, and some batches large enough for the capped launches."""
-    bands = {next(j for j, (lo, hi) in enumerate(CHUNK_BANDS) if lo <= c["H"] // 8 <= hi) for c in PROBLEMS}
+    P = DEFAULT_PROBLEMS
+    bands = {next(j for j, (lo, hi) in enumerate(CHUNK_BANDS) if lo <= c["H"] // 8 <= hi) for c in P}
     assert bands == set(range(len(CHUNK_BANDS)))
-    assert {c["act"] for c in PROBLEMS} == {synth.F16, synth.BF16}
-    assert any(c["maxrep"] for c in PROBLEMS) and any(not c["maxrep"] for c in PROBLEMS)
-    assert any(c["E"] > 128 for c in PROBLEMS) and any(c["E"] <= 16 for c in PROBLEMS)
-    assert any(c["T"] * c["k"] >= 4096 and c["H"] > 1024 for c in PROBLEMS)
+    assert {c["act"] for c in P} == {synth.F16, synth.BF16}
+    assert any(c["maxrep"] for c in P) and any(not c["maxrep"] for c in P)
+    assert any(c["E"] > 128 for c in P) and any(c["E"] <= 16 for c in P)
+    assert any(c["T"] * c["k"] >= 4096 and c["H"] > 1024 for c in P)
 
 
 @pytest.mark.gpu
