@@ -225,15 +225,17 @@ def test_backward_empty_batch_and_errors():
     assert ei.value.status == B.MOE_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("w", [synth.DECODE, synth.TRAIN_TOP2, synth.TRAIN_TOP6, synth.LARGE],
-                         ids=lambda w: w.name)
-def test_backward_full_size(w):
+# every workload at seeds 0 and 1
+FULL_CASES = [(w, s) for w in (synth.DECODE, synth.TRAIN_TOP2, synth.TRAIN_TOP6, synth.LARGE) for s in (0, 1)]
+
+
+@pytest.mark.parametrize("w,seed", FULL_CASES, ids=lambda v: v.name if hasattr(v, "name") else f"seed{v}")
+def test_backward_full_size(w, seed):
     """Full size, every element, token chunk by token chunk: dy bit for bit,
     dw within its fp32 summation bound and dx (from dsend = dy) within
     1e-3 + 4e-3 |ref| against the oracle; and dx against the property
     sum_j w_j = 1 (dx = dout up to the roundings of dy, the fp32 sum and dx)."""
-    say(f"[case] backward full {w.name}")
-    seed = 0
+    say(f"[case] backward full {w.name} seed {seed}")
     logits, x = synth.make_logits(w, seed), synth.make_x(w, seed)
     rep = synth.replica_table(w)
     ref = oracle.route_and_layout(w.T, w.E, w.k, w.R, logits, rep)

@@ -29,11 +29,13 @@ def dispatch_identity_all_rows(b, k):
         assert torch.equal(b.send[r0:r1].view(torch.int16), b.x.index_select(0, tok).view(torch.int16)), r0
 
 
-@pytest.mark.parametrize("w", [synth.DECODE, synth.TRAIN_TOP2, synth.TRAIN_TOP6, synth.LARGE],
-                         ids=lambda w: w.name)
-def test_full_size(w):
-    seed = 0
-    say(f"[case] full {w.name}")
+# every workload at seeds 0-2
+FULL_CASES = [(w, s) for w in (synth.DECODE, synth.TRAIN_TOP2, synth.TRAIN_TOP6, synth.LARGE) for s in (0, 1, 2)]
+
+
+@pytest.mark.parametrize("w,seed", FULL_CASES, ids=lambda v: v.name if hasattr(v, "name") else f"seed{v}")
+def test_full_size(w, seed):
+    say(f"[case] full {w.name} seed {seed}")
     logits = synth.make_logits(w, seed)
     x = synth.make_x(w, seed)
     rep = synth.replica_table(w)
