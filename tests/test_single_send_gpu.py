@@ -192,11 +192,12 @@ def test_single_send_empty_batch():
     assert host(b.dedup).tolist() == [0] * 4
 
 
+@pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("w", [synth.DECODE, synth.TRAIN_TOP2, synth.TRAIN_TOP6, synth.LARGE],
                          ids=lambda w: w.name)
-def test_single_send_full_size(w):
-    say(f"[case] single-send full {w.name}")
-    logits, x = synth.make_logits(w, 0), synth.make_x(w, 0)
+def test_single_send_full_size(w, seed):
+    say(f"[case] single-send full {w.name} seed {seed}")
+    logits, x = synth.make_logits(w, seed), synth.make_x(w, seed)
     rep = synth.replica_table(w)
     ref = oracle.route_and_layout(w.T, w.E, w.k, w.R, logits, rep)
     b, ss, ex = run_single_send(w, logits, x, rep)

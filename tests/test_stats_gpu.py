@@ -57,10 +57,11 @@ def test_stats_small(w, seed):
     run_stats(w, seed)
 
 
+@pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("w", [synth.DECODE, synth.TRAIN_TOP2, synth.TRAIN_TOP6, synth.LARGE],
                          ids=lambda w: w.name)
-def test_stats_full_size(w):
-    got = run_stats(w, 0)
+def test_stats_full_size(w, seed):
+    got = run_stats(w, seed)
     say(f"  max/mean {got[0]:.4f} gini {got[1]:.4f} alpha {got[2]:.2f} locality {got[3]:.4f}")
 
 
